@@ -1,0 +1,390 @@
+/*
+ * kev_oracle.c -- plain fp64 CPU oracle for segment-isolated packed attention.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only tests/, the smoke check and
+ * the bench's cpu_baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library and includes nothing from it.
+ *
+ * What it computes (written out as the plain definition, no tiling, no
+ * online softmax, no reordering):
+ *
+ *   Inference-engine primer (sakurs2.com), section 2.1: causal self-attention
+ *     Z = softmax(Q K^T / sqrt(d_h) + M) V,  M_ij = 0 if j <= i else -inf,
+ *   with the softmax taken along each row.
+ *
+ *   Kev article (icman.com.cn), sections 2.1 and 2.3: several questions are
+ *   packed into one token stream; question s occupies an interval of the
+ *   stream and the mask is the AND of the causal mask and the block-diagonal
+ *   isolation mask.  Intervals are read as half-open [cu[s], cu[s+1]), which
+ *   is how the article's code slices them (start:end with end = start + len).
+ *
+ *   So for row i of segment [a, b), query head h and key/value head g:
+ *     s_j   = (sum_c q[i,h,c] k[j,g,c]) / sqrt(d)        for a <= j <= i
+ *     m     = max_j s_j
+ *     w_j   = exp(s_j - m),  Z = sum_j w_j                (stable softmax,
+ *                                                          primer section 2.4)
+ *     out[i,h,c] = (sum_j w_j v[j,g,c]) / Z
+ *   Positions where M = -inf are never visited, so their weight is exactly 0.
+ *
+ *   Grouped KV heads are not named on the pages; q head h reads KV head
+ *   h / (heads / kv_heads), i.e. each KV head is logically repeated for a
+ *   contiguous group of query heads (the KV-cache isolation article,
+ *   hnwysp.cn, section 7.1, contrasts such a shared view with a copy).
+ *
+ *   Decode (primer section 2.2): the new query attends over the cached K/V
+ *   plus the new token's K/V with no mask; the cache is written in place
+ *   rather than concatenated.  Each request owns one fixed-capacity slot of
+ *   a pre-allocated pool (Kev part 2, gsyq.cn, section 2.2).  The pool layout
+ *   is [slot][K or V][kv head][position][d], the per-head cache
+ *   [B, H, S_cache, d] of the isolation article's section 2.2 with slots in
+ *   place of the batch.  cache_lens[r] counts the tokens in the slot after
+ *   the append, so the sequence is pool rows 0..L-2 followed by k_new/v_new
+ *   at position L-1.
+ *
+ * Inputs are the exact bits the GPU path sees (bf16 bits or fp32), widened
+ * to double.  Outputs are double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_BF16 0
+#define ORACLE_F32 1
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG -1
+#define ORACLE_BAD_SEQLENS -3
+#define ORACLE_SLOT_OVERFLOW -4
+#define ORACLE_BAD_SLOT -5
+#define ORACLE_NO_MEMORY -7
+
+static double widen(const void *base, int dtype, size_t idx)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static void put_threads(int n_threads)
+{
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+}
+
+int kev_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Plain softmax attention of one query vector over n key/value vectors.
+ *   qv[d], kv[j*d + c], vv[j*d + c] (already widened), w[n] is scratch.
+ *   out[c] = sum_j softmax_j(q.k_j / sqrt(d)) v_j[c]
+ */
+static void attend(const double *qv, const double *kv, const double *vv, int n, int d,
+                   double *w, double *out)
+{
+    double scale = 1.0 / sqrt((double)d);
+    double m = -INFINITY;
+    for (int j = 0; j < n; j++) {
+        double s = 0.0;
+        for (int c = 0; c < d; c++)
+            s += qv[c] * kv[(size_t)j * d + c];
+        w[j] = s * scale;
+        if (w[j] > m)
+            m = w[j];
+    }
+    double z = 0.0;
+    for (int j = 0; j < n; j++) {
+        w[j] = exp(w[j] - m);
+        z += w[j];
+    }
+    for (int c = 0; c < d; c++) {
+        double acc = 0.0;
+        for (int j = 0; j < n; j++)
+            acc += w[j] * vv[(size_t)j * d + c];
+        out[c] = acc / z;
+    }
+}
+
+static int check_seqlens(const int32_t *cu, int32_t n_seg)
+{
+    if (n_seg < 0 || (n_seg > 0 && cu == NULL))
+        return ORACLE_BAD_ARG;
+    if (n_seg == 0)
+        return ORACLE_OK;
+    if (cu[0] != 0)
+        return ORACLE_BAD_SEQLENS;
+    for (int32_t s = 0; s < n_seg; s++)
+        if (cu[s + 1] < cu[s])
+            return ORACLE_BAD_SEQLENS;
+    return ORACLE_OK;
+}
+
+static int check_heads(int32_t heads, int32_t kv_heads, int32_t d, int dtype)
+{
+    if (heads <= 0 || kv_heads <= 0 || d <= 0 || heads % kv_heads != 0)
+        return ORACLE_BAD_ARG;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F32)
+        return ORACLE_BAD_ARG;
+    return ORACLE_OK;
+}
+
+/*
+ * Output rows [i0, i1) of query head h, all inside segment [a, b).
+ * Row i attends keys a..i of KV head h / G.  The segment's K and V for that
+ * head are widened once (rows a..i1-1) and each row uses its causal prefix.
+ */
+static void segment_head(const void *q, const void *k, const void *v, int dtype,
+                         int32_t a, int32_t i0, int32_t i1, int32_t h,
+                         int32_t heads, int32_t kv_heads, int32_t d,
+                         double *kbuf, double *vbuf, double *qv, double *w,
+                         double *out /* rows i0..i1-1, [row][d] */)
+{
+    int32_t g = h / (heads / kv_heads);
+    int32_t n = i1 - a;
+    for (int32_t j = 0; j < n; j++)
+        for (int32_t c = 0; c < d; c++) {
+            size_t src = ((size_t)(a + j) * kv_heads + g) * d + c;
+            kbuf[(size_t)j * d + c] = widen(k, dtype, src);
+            vbuf[(size_t)j * d + c] = widen(v, dtype, src);
+        }
+    for (int32_t i = i0; i < i1; i++) {
+        for (int32_t c = 0; c < d; c++)
+            qv[c] = widen(q, dtype, ((size_t)i * heads + h) * d + c);
+        attend(qv, kbuf, vbuf, i - a + 1, d, w, out + (size_t)(i - i0) * d);
+    }
+}
+
+/*
+ * Full packed prefill.
+ *   q[T, heads, d], k/v[T, kv_heads, d] (bf16 bits or fp32), cu[n_seg+1].
+ *   out[T, heads, d] double.  Threads take (segment, head) units.
+ */
+int kev_oracle_prefill(const void *q, const void *k, const void *v, int dtype,
+                       const int32_t *cu, int32_t n_seg, int32_t heads, int32_t kv_heads,
+                       int32_t d, double *out, int n_threads)
+{
+    int rc = check_seqlens(cu, n_seg);
+    if (rc)
+        return rc;
+    rc = check_heads(heads, kv_heads, d, dtype);
+    if (rc)
+        return rc;
+    if (n_seg == 0)
+        return ORACLE_OK;
+    int32_t maxlen = 0;
+    for (int32_t s = 0; s < n_seg; s++)
+        if (cu[s + 1] - cu[s] > maxlen)
+            maxlen = cu[s + 1] - cu[s];
+    long units = (long)n_seg * heads;
+    int fail = 0;
+    put_threads(n_threads);
+#pragma omp parallel
+    {
+        double *kbuf = malloc(sizeof(double) * ((size_t)maxlen * d + 1));
+        double *vbuf = malloc(sizeof(double) * ((size_t)maxlen * d + 1));
+        double *seg_out = malloc(sizeof(double) * ((size_t)maxlen * d + 1));
+        double *qv = malloc(sizeof(double) * d);
+        double *w = malloc(sizeof(double) * ((size_t)maxlen + 1));
+        if (!kbuf || !vbuf || !seg_out || !qv || !w) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long u = 0; u < units; u++) {
+                int32_t s = (int32_t)(u / heads), h = (int32_t)(u % heads);
+                int32_t a = cu[s], b = cu[s + 1];
+                if (b == a)
+                    continue;
+                segment_head(q, k, v, dtype, a, a, b, h, heads, kv_heads, d,
+                             kbuf, vbuf, qv, w, seg_out);
+                for (int32_t i = a; i < b; i++)
+                    memcpy(out + ((size_t)i * heads + h) * d, seg_out + (size_t)(i - a) * d,
+                           sizeof(double) * d);
+            }
+        }
+        free(kbuf);
+        free(vbuf);
+        free(seg_out);
+        free(qv);
+        free(w);
+    }
+    return fail ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/*
+ * Sampled outputs of the packed prefill: for each n, out_rows[n, :] is the
+ * output of token rows[n] at query head row_heads[n].  Same arithmetic as
+ * the full call; used where the full oracle would take too long.
+ */
+int kev_oracle_prefill_rows(const void *q, const void *k, const void *v, int dtype,
+                            const int32_t *cu, int32_t n_seg, int32_t heads, int32_t kv_heads,
+                            int32_t d, const int32_t *rows, const int32_t *row_heads,
+                            int32_t n_rows, double *out_rows, int n_threads)
+{
+    int rc = check_seqlens(cu, n_seg);
+    if (rc)
+        return rc;
+    rc = check_heads(heads, kv_heads, d, dtype);
+    if (rc)
+        return rc;
+    int32_t T = n_seg > 0 ? cu[n_seg] : 0;
+    for (int32_t n = 0; n < n_rows; n++)
+        if (rows[n] < 0 || rows[n] >= T || row_heads[n] < 0 || row_heads[n] >= heads)
+            return ORACLE_BAD_ARG;
+    int fail = 0;
+    put_threads(n_threads);
+#pragma omp parallel
+    {
+        size_t cap = 0;
+        double *kbuf = NULL, *vbuf = NULL, *w = NULL;
+        double *qv = malloc(sizeof(double) * d);
+        if (!qv) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int32_t n = 0; n < n_rows; n++) {
+            if (!qv)
+                continue;
+            int32_t i = rows[n];
+            /* the last segment s with cu[s] <= i; then cu[s+1] > i */
+            int32_t lo = 0, hi = n_seg - 1;
+            while (lo < hi) {
+                int32_t mid = (lo + hi + 1) / 2;
+                if (cu[mid] <= i)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            int32_t a = cu[lo];
+            size_t need = (size_t)(i - a + 1);
+            if (need > cap) {
+                free(kbuf);
+                free(vbuf);
+                free(w);
+                kbuf = malloc(sizeof(double) * need * d);
+                vbuf = malloc(sizeof(double) * need * d);
+                w = malloc(sizeof(double) * need);
+                cap = need;
+                if (!kbuf || !vbuf || !w) {
+#pragma omp atomic write
+                    fail = 1;
+                    cap = 0;
+                    continue;
+                }
+            }
+            segment_head(q, k, v, dtype, a, i, i + 1, row_heads[n], heads, kv_heads, d,
+                         kbuf, vbuf, qv, w, out_rows + (size_t)n * d);
+        }
+        free(kbuf);
+        free(vbuf);
+        free(w);
+        free(qv);
+    }
+    return fail ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/*
+ * Single-token decode against the slot pool.
+ *   q[n_req, heads, d], k_new/v_new[n_req, kv_heads, d],
+ *   pool[n_slots][2][kv_heads][capacity][d], slot_ids[n_req], cache_lens[n_req].
+ *   out[n_req, heads, d] double.
+ * If pool_after is not NULL it receives a copy of the pool with row L-1 of
+ * each request's slot replaced by k_new / v_new (the expected pool after
+ * the in-place append); it must have the pool's size and element type.
+ */
+int kev_oracle_decode(const void *q, const void *pool, int32_t n_slots, int32_t capacity,
+                      int32_t kv_heads, int32_t d, const int32_t *slot_ids,
+                      const int32_t *cache_lens, const void *k_new, const void *v_new,
+                      int32_t n_req, int32_t heads, int dtype, double *out, void *pool_after,
+                      int n_threads)
+{
+    int rc = check_heads(heads, kv_heads, d, dtype);
+    if (rc)
+        return rc;
+    if (n_req < 0 || n_slots <= 0 || capacity <= 0)
+        return ORACLE_BAD_ARG;
+    for (int32_t r = 0; r < n_req; r++) {
+        if (slot_ids[r] < 0 || slot_ids[r] >= n_slots)
+            return ORACLE_BAD_SLOT;
+        if (cache_lens[r] < 1 || cache_lens[r] > capacity)
+            return ORACLE_SLOT_OVERFLOW;
+        for (int32_t r2 = 0; r2 < r; r2++)
+            if (slot_ids[r2] == slot_ids[r])
+                return ORACLE_BAD_SLOT;
+    }
+    size_t esz = dtype == ORACLE_F32 ? 4 : 2;
+    size_t plane = (size_t)capacity * d;                 /* one (slot, K|V, head) */
+    size_t slot_elems = (size_t)2 * kv_heads * plane;
+    int G = heads / kv_heads;
+    long units = (long)n_req * heads;
+    int fail = 0;
+    put_threads(n_threads);
+#pragma omp parallel
+    {
+        double *kbuf = malloc(sizeof(double) * plane);
+        double *vbuf = malloc(sizeof(double) * plane);
+        double *qv = malloc(sizeof(double) * d);
+        double *w = malloc(sizeof(double) * capacity);
+        if (!kbuf || !vbuf || !qv || !w) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long u = 0; u < units; u++) {
+                int32_t r = (int32_t)(u / heads), h = (int32_t)(u % heads), g = h / G;
+                int32_t L = cache_lens[r];
+                size_t kbase = (size_t)slot_ids[r] * slot_elems + (size_t)g * plane;
+                size_t vbase = kbase + (size_t)kv_heads * plane;
+                for (int32_t j = 0; j < L - 1; j++)
+                    for (int32_t c = 0; c < d; c++) {
+                        kbuf[(size_t)j * d + c] = widen(pool, dtype, kbase + (size_t)j * d + c);
+                        vbuf[(size_t)j * d + c] = widen(pool, dtype, vbase + (size_t)j * d + c);
+                    }
+                for (int32_t c = 0; c < d; c++) {
+                    size_t src = ((size_t)r * kv_heads + g) * d + c;
+                    kbuf[(size_t)(L - 1) * d + c] = widen(k_new, dtype, src);
+                    vbuf[(size_t)(L - 1) * d + c] = widen(v_new, dtype, src);
+                    qv[c] = widen(q, dtype, ((size_t)r * heads + h) * d + c);
+                }
+                attend(qv, kbuf, vbuf, L, d, w, out + ((size_t)r * heads + h) * d);
+            }
+        }
+        free(kbuf);
+        free(vbuf);
+        free(qv);
+        free(w);
+    }
+    if (fail)
+        return ORACLE_NO_MEMORY;
+    if (pool_after) {
+        memcpy(pool_after, pool, esz * slot_elems * (size_t)n_slots);
+        for (int32_t r = 0; r < n_req; r++)
+            for (int32_t g = 0; g < kv_heads; g++) {
+                size_t kdst = (size_t)slot_ids[r] * slot_elems + (size_t)g * plane +
+                              (size_t)(cache_lens[r] - 1) * d;
+                size_t vdst = kdst + (size_t)kv_heads * plane;
+                size_t src = ((size_t)r * kv_heads + g) * d;
+                memcpy((char *)pool_after + kdst * esz, (const char *)k_new + src * esz, esz * d);
+                memcpy((char *)pool_after + vdst * esz, (const char *)v_new + src * esz, esz * d);
+            }
+    }
+    return ORACLE_OK;
+}
