@@ -1,0 +1,215 @@
+"""Benchmark of the packed-prefill + slot-decode hot path on one MI355X.
+
+One step = one packed prefill over the Qwen2.5-7B-shaped workload (bf16, 28 q / 4 kv
+heads, head_dim 128, 8 questions with lengths uniform in [256, 2048], seed 42) followed
+by one slot-pool decode (bf16, 32 q / 8 kv heads, 64 requests, slot capacity 2458,
+80-slot pool, new K/V appended in-kernel, seed 44).  Between the two a 512 MiB buffer is
+written so the decode reads its KV rows from HBM rather than from the 256 MB MALL.
+
+Prints ONE JSON line.  `value` is the prefill's effective TFLOP/s (only unmasked score
+entries counted: 4 * d * heads * sum L(L+1)/2 FLOPs per call) over the average duration
+of the prefill call measured with HIP events on the launch stream.  The decode's
+achieved HBM GB/s (algorithmic bytes over event-timed duration) is reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBPS = 8000.0        # MI355X published HBM3E bandwidth
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def traffic_for(kernel: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, if the kernel is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("source_sha256") != src_hash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def source_hash(files) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "segment_isolated_packed_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def cpu_baseline(case, budget_s: float = 20.0) -> dict:
+    """The oracle as it stands, timed on the host cores on a bounded sample of the workload:
+    all questions, the query heads of KV head 0 only."""
+    import oracle
+    orc = oracle.get()
+    G = case.heads // case.kv_heads
+    q = case.q[:, :G].copy()
+    k = case.k[:, :1].copy()
+    v = case.v[:, :1].copy()
+    t0 = time.perf_counter()
+    orc.prefill(q, k, v, case.cu_seqlens, G, 1, case.head_dim, case.dtype)
+    dt = time.perf_counter() - t0
+    flops = case.effective_flops() * G / case.heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": orc.max_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle, all {case.n_seg} questions of the workload, query heads "
+                      f"0..{G - 1} (KV head 0), {flops / 1e9:.1f} GFLOP effective, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen25_7b",
+                    choices=["qwen25_7b", "qwen3_8b", "skewed_long"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one half of the step (profiling runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU; the path shards by question or KV head "
+              "with no exchange step, and multi-GPU runs are not part of it (use --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import segment_isolated_packed_amd as K
+    from segment_isolated_packed_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+
+    def to_dev(a, dtype):
+        if dtype == W.BF16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    log(f"generating {args.workload} prefill inputs")
+    pc = W.prefill_case(args.workload)
+    q, k, v = (to_dev(x, pc.dtype) for x in (pc.q, pc.k, pc.v))
+    cu = torch.from_numpy(pc.cu_seqlens).to(dev)
+    out = torch.empty_like(q)
+    log("generating slot-decode inputs")
+    dc = W.make_decode()
+    dq, dpool, dkn, dvn = (to_dev(x, dc.dtype) for x in (dc.q, dc.pool, dc.k_new, dc.v_new))
+    dids = torch.from_numpy(dc.slot_ids).to(dev)
+    dlens = torch.from_numpy(dc.cache_lens).to(dev)
+    dout = torch.empty_like(dq)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    do_pre = args.only in (None, "prefill")
+    do_dec = args.only in (None, "decode")
+
+    def step(ev=None):
+        if do_pre:
+            if ev: ev[0].record(stream)
+            K.kev_packed_attn_prefill(q, k, v, cu, out=out)
+            if ev: ev[1].record(stream)
+        if do_dec:
+            if not args.no_flush:
+                flush_buf.fill_(1)
+            if ev: ev[2].record(stream)
+            K.kev_slot_attn_decode(dq, dpool, dids, dlens, dkn, dvn, out=dout)
+            if ev: ev[3].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    errs = K.kev_get_device_errors()
+    if errs:
+        raise RuntimeError(f"device error flags {errs}")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log("timed region done")
+
+    pre_ms = [e[0].elapsed_time(e[1]) for e in events] if do_pre else [float("nan")]
+    dec_ms = [e[2].elapsed_time(e[3]) for e in events] if do_dec else [float("nan")]
+    pre_avg = float(np.mean(pre_ms))
+    dec_avg = float(np.mean(dec_ms))
+    flops = pc.effective_flops()
+    dbytes = dc.algorithmic_bytes()
+    tflops = flops / (pre_avg * 1e-3) / 1e12 if do_pre else None
+    gbps = dbytes / (dec_avg * 1e-3) / 1e9 if do_dec else None
+
+    pre_hash = source_hash(["kev_prefill_bf16.hip", "kev_schedule.hip", "kev_api.hip"])
+    dec_hash = source_hash(["kev_decode.hip", "kev_api.hip"])
+    result = {
+        "metric": "effective TFLOP/s packed prefill (% MFMA peak); decode HBM GB/s (% peak)",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v, lengths per the workload recipe)",
+        "config": {
+            "workload": f"{args.workload} packed prefill + slot-pool decode",
+            "prefill": W.PREFILL_DESCRIPTIONS[args.workload],
+            "prefill_seed": pc.seed,
+            "prefill_tokens": pc.total_tokens,
+            "prefill_effective_gflop": flops / 1e9,
+            "decode": W.DECODE_DESCRIPTION,
+            "decode_seed": dc.seed,
+            "decode_algorithmic_mb": dbytes / 1e6,
+            "step": "prefill call (scheduler + attention kernel), 512 MiB flush write, decode call",
+        },
+        "prefill_ms": pre_avg,
+        "prefill_pct_peak": tflops / PEAK_BF16_TFLOPS * 100 if tflops else None,
+        "roofline": {
+            "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / PEAK_BF16_TFLOPS if tflops else None,
+            "traffic": traffic_for("prefill_bf16_kernel", pre_hash),
+            "kernel": "kev schedule_kernel + prefill_bf16_kernel<128,7> (one prefill call)",
+            "algorithmic_flops_per_launch": flops,
+        },
+        "decode": {
+            "value": gbps, "unit": "GB/s", "ms": dec_avg,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": gbps / PEAK_HBM_GBPS if gbps else None,
+                         "traffic": traffic_for("decode_bf16_kernel", dec_hash),
+                         "algorithmic_bytes_per_launch": dbytes},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(pc)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * kev.h -- C ABI of the segment-isolated packed attention library (gfx950).
+ *
+ * Two entry points:
+ *
+ *   kev_packed_attn_prefill  packed prefill.  Several independent questions
+ *       are concatenated into one token stream and each token attends only to
+ *       earlier-or-equal positions of its own question:
+ *           Z = softmax(Q K^T / sqrt(d_h) + M) V
+ *       with M_ij = 0 when j <= i and i, j lie in the same question interval,
+ *       and -inf otherwise.  The formula and the causal mask are those of the
+ *       inference-engine primer (sakurs2.com, section 2.1); the mask is the
+ *       AND of the causal lower triangle and the block-diagonal isolation mask
+ *       of the Kev article (icman.com.cn, sections 2.1 and 2.3), and the
+ *       question intervals are handed over in flash-attn's varlen cu_seqlens
+ *       form rather than as a dense matrix (same article, sections 5.2, 6.4).
+ *
+ *   kev_slot_attn_decode  single-token decode against a pre-allocated KV pool
+ *       cut into fixed-capacity slots, one slot per question (Kev part 2,
+ *       gsyq.cn, section 2.2).  The new token's K/V are written into the slot
+ *       in place, not concatenated (primer, section 2.2), and the new query
+ *       attends over all cached positions with no mask (same section).
+ *
+ * Conventions shared by every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller, contiguous in
+ *     the layouts stated below, never freed or retained by the library.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL means the default stream): they validate, enqueue and return.
+ *   - Arguments that can be checked without reading device memory are checked
+ *     before any HIP call; a failing check returns a negative kev_status and
+ *     enqueues nothing.  n_seg == 0 or n_req == 0 is a successful no-op.
+ *   - Device-array contents (cu_seqlens, slot_ids, cache_lens) are guarded in
+ *     the kernels: an invalid unit is skipped (its outputs are left untouched,
+ *     nothing out of range is read or written) and a bit is set in the
+ *     per-device error word read by kev_get_device_errors.  With the
+ *     environment variable KEV_CHECK=1 they are also copied to the host and
+ *     checked synchronously before launch, returning the matching status.
+ *   - Each (device, stream) pair gets its own workspace, allocated by the
+ *     library on first use and grown when needed (this may synchronise the
+ *     device).  Calls on one stream are ordered; calls on different streams
+ *     do not share workspace.
+ *   - Head grouping: query head h reads KV head h / (heads / kv_heads).
+ */
+#ifndef KEV_H
+#define KEV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KEV_BF16 = 0, KEV_F32 = 1 } kev_dtype;
+
+typedef enum {
+    KEV_OK = 0,
+    KEV_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, heads % kv_heads != 0 */
+    KEV_ERR_UNSUPPORTED = -2,   /* dtype / head_dim combination not built */
+    KEV_ERR_BAD_SEQLENS = -3,   /* cu_seqlens not 0-based, decreasing, or != total_tokens at the end */
+    KEV_ERR_SLOT_OVERFLOW = -4, /* a cache length outside [1, capacity] */
+    KEV_ERR_BAD_SLOT = -5,      /* a slot id outside [0, n_slots), or repeated within one call */
+    KEV_ERR_DEVICE = -6,        /* a HIP call failed */
+    KEV_ERR_NO_MEMORY = -7      /* workspace allocation failed */
+} kev_status;
+
+/* Bits of the per-device error word (kev_get_device_errors). */
+#define KEV_DEVERR_SEQLENS 1u   /* cu_seqlens invalid; the prefill call computed nothing */
+#define KEV_DEVERR_SLOT 2u      /* a request's slot id was out of range; request skipped */
+#define KEV_DEVERR_CACHE_LEN 4u /* a request's cache length was outside [1, capacity]; skipped */
+
+/*
+ * Packed, segment-isolated causal prefill.
+ *
+ *   q            [total_tokens, heads, head_dim]      dtype
+ *   k, v         [total_tokens, kv_heads, head_dim]   dtype (already position-encoded)
+ *   cu_seqlens   int32 [n_seg + 1], device; cu[0] = 0, non-decreasing,
+ *                cu[n_seg] = total_tokens; question s owns tokens
+ *                [cu[s], cu[s+1]) (half-open; empty questions are allowed)
+ *   out          [total_tokens, heads, head_dim]      dtype, written for every token
+ *   total_tokens the host's copy of cu[n_seg] (bounds the launch and the workspace)
+ *   dtype        KEV_BF16 (head_dim 64 or 128; bf16 MFMA, fp32 accumulation and
+ *                softmax, output rounded to nearest even) or KEV_F32
+ *                (head_dim 16, 32, 64 or 128; fp32 arithmetic throughout)
+ *
+ * The scale is fixed at 1/sqrt(head_dim); there is no bias, dropout or softcap.
+ * No dense mask is built: a scheduler kernel lists the (question, query block)
+ * work items from cu_seqlens and the attention kernel visits only key blocks
+ * at or left of each block's diagonal inside its own question.
+ * Returns KEV_OK or a negative kev_status.
+ */
+int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
+                            const int32_t *cu_seqlens, int32_t n_seg,
+                            int32_t heads, int32_t kv_heads, int32_t head_dim,
+                            void *out, int32_t total_tokens, int32_t dtype, void *stream);
+
+/*
+ * KV slot pool geometry.  `data` is a caller-owned device buffer laid out as
+ *   [n_slots][2][kv_heads][capacity][head_dim]      (index 0 = K, 1 = V)
+ * i.e. each slot is one contiguous block holding a per-head cache
+ * [kv_heads][capacity][head_dim] for K followed by the same for V.
+ */
+typedef struct {
+    void *data;
+    int32_t n_slots;
+    int32_t capacity;
+    int32_t kv_heads;
+    int32_t head_dim;
+    int32_t dtype; /* kev_dtype; KEV_BF16 only */
+} kev_kv_pool;
+
+/*
+ * Single-token decode over the slot pool, with in-kernel append.
+ *
+ *   q            [n_req, heads, head_dim]          bf16
+ *   kv_pool      host pointer to the pool descriptor (read during the call only)
+ *   slot_ids     int32 [n_req], device; distinct slots in [0, n_slots)
+ *   cache_lens   int32 [n_req], device; tokens in the slot AFTER the append,
+ *                in [1, capacity] (1 = empty cache before this step)
+ *   out          [n_req, heads, head_dim]          bf16
+ *   k_new, v_new [n_req, kv_heads, head_dim]       bf16
+ *
+ * For request r with slot s = slot_ids[r] and L = cache_lens[r]: row L-1 of
+ * slot s (K and V, every KV head) is overwritten with k_new[r] / v_new[r];
+ * then query r attends over rows 0..L-1 of slot s.  No other pool byte is
+ * written.  Repeated slot ids in one call are undefined behaviour (rejected
+ * with KEV_ERR_BAD_SLOT under KEV_CHECK=1).  A slot is never truncated or
+ * re-laid out: a length past capacity is an error, not a reallocation.
+ * head_dim must be 64 or 128 and equal to the pool's.
+ */
+int kev_slot_attn_decode(const void *q, const kev_kv_pool *kv_pool,
+                         const int32_t *slot_ids, const int32_t *cache_lens, void *out,
+                         const void *k_new, const void *v_new, int32_t n_req, int32_t heads,
+                         void *stream);
+
+/* Human-readable text for a kev_status value (static storage). */
+const char *kev_status_string(int status);
+
+/*
+ * Synchronises `stream`, then reads and clears the error word of the current
+ * device into *flags_out (a KEV_DEVERR_* bitmask, 0 if every unit was valid).
+ */
+int kev_get_device_errors(void *stream, int32_t *flags_out);
+
+/*
+ * Schedule inspection (tests and tuning).
+ *
+ * kev_prefill_block_rows: query rows per work item that a prefill call with
+ * these arguments uses (0 if the combination is unsupported).
+ *
+ * kev_schedule_host: the work list computed on the host from a HOST copy of
+ * cu_seqlens: items_out[2*i] = question, items_out[2*i+1] = query block, in
+ * the order the device scheduler uses (query block descending, so the
+ * longest items start first).  Returns KEV_OK and *n_items_out, or
+ * KEV_ERR_INVALID_ARG if max_items is too small.
+ *
+ * kev_schedule_device: runs the device scheduler kernel on device cu_seqlens
+ * and copies its work list to the host buffer items_out (synchronises).
+ */
+int kev_prefill_block_rows(int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype);
+int kev_schedule_host(const int32_t *cu_seqlens_host, int32_t n_seg, int32_t block_rows,
+                      int32_t *items_out, int32_t max_items, int32_t *n_items_out);
+int kev_schedule_device(const int32_t *cu_seqlens, int32_t n_seg, int32_t total_tokens,
+                        int32_t block_rows, int32_t *items_out, int32_t max_items,
+                        int32_t *n_items_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KEV_H */

@@ -1,0 +1,363 @@
+// kev_api.hip -- the C ABI: argument checks, per-stream workspace, launches.
+//
+// Everything host-checkable is checked before the first HIP call.  The
+// boundary follows the pages' statement of the problem: the packed stream plus
+// question intervals in cu_seqlens form, never a dense mask (Kev article,
+// icman.com.cn, sections 2.2, 5.2, 6.4); one fixed-capacity slot per question
+// in a caller-owned pool that is passed in explicitly rather than held as
+// hidden state (Kev part 2, gsyq.cn, section 2.2; KV-cache isolation article,
+// hnwysp.cn, section 3.3); and a slot that would overflow is an error, never a
+// re-layout (Kev part 2, section 4.2).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "../../include/kev.h"
+#include "kev_internal.h"
+
+namespace {
+
+using namespace kev;
+
+struct Buffer {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
+struct State {
+    std::mutex mu;
+    std::map<int, int32_t *> err_word;                        // device -> error word
+    std::map<std::pair<int, void *>, Buffer> sched_ws;        // (device, stream)
+    std::map<std::pair<int, void *>, Buffer> decode_ws;       // (device, stream), zeroed counters
+};
+
+State &state() {
+    static State *s = new State();   // never destroyed: outlives static teardown order
+    return *s;
+}
+
+bool check_enabled() {
+    const char *e = std::getenv("KEV_CHECK");
+    return e && e[0] == '1';
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? KEV_OK : KEV_ERR_DEVICE; }
+
+// Device error word of the current device (allocated and zeroed on first use).
+int error_word(int dev, int32_t **out) {
+    State &st = state();
+    std::lock_guard<std::mutex> lock(st.mu);
+    auto it = st.err_word.find(dev);
+    if (it != st.err_word.end()) {
+        *out = it->second;
+        return KEV_OK;
+    }
+    int32_t *p = nullptr;
+    if (hipMalloc(&p, 256) != hipSuccess) return KEV_ERR_NO_MEMORY;
+    if (hipMemset(p, 0, 256) != hipSuccess) return KEV_ERR_DEVICE;
+    st.err_word[dev] = p;
+    *out = p;
+    return KEV_OK;
+}
+
+// Workspace of at least `bytes` for (device, stream).  Grown buffers are zeroed
+// on the stream before first use; decode relies on its counters starting at 0
+// and returns them to 0 itself.
+int workspace(std::map<std::pair<int, void *>, Buffer> &m, int dev, hipStream_t stream,
+              size_t bytes, void **out) {
+    State &st = state();
+    std::lock_guard<std::mutex> lock(st.mu);
+    Buffer &b = m[{dev, (void *)stream}];
+    if (b.bytes < bytes) {
+        if (b.ptr) {
+            if (hipStreamSynchronize(stream) != hipSuccess) return KEV_ERR_DEVICE;
+            if (hipFree(b.ptr) != hipSuccess) return KEV_ERR_DEVICE;
+            b.ptr = nullptr;
+            b.bytes = 0;
+        }
+        size_t want = std::max(bytes, (size_t)1 << 16);
+        if (hipMalloc(&b.ptr, want) != hipSuccess) {
+            b.ptr = nullptr;
+            return KEV_ERR_NO_MEMORY;
+        }
+        if (hipMemsetAsync(b.ptr, 0, want, stream) != hipSuccess) return KEV_ERR_DEVICE;
+        b.bytes = want;
+    }
+    *out = b.ptr;
+    return KEV_OK;
+}
+
+bool prefill_supported(int32_t head_dim, int32_t dtype) {
+    if (dtype == KEV_BF16) return head_dim == 64 || head_dim == 128;
+    if (dtype == KEV_F32) return head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128;
+    return false;
+}
+
+int32_t block_rows_for(int32_t heads, int32_t kv_heads, int32_t dtype) {
+    if (dtype == KEV_F32) return kF32BlockRows;
+    return prefill_shape_bf16(heads, kv_heads).block_rows;
+}
+
+int host_check_seqlens(const int32_t *cu, int32_t n_seg, int32_t total_tokens) {
+    if (cu[0] != 0 || cu[n_seg] != total_tokens) return KEV_ERR_BAD_SEQLENS;
+    for (int32_t s = 0; s < n_seg; ++s)
+        if (cu[s + 1] < cu[s]) return KEV_ERR_BAD_SEQLENS;
+    return KEV_OK;
+}
+
+// Schedule on the device into the (device, stream) workspace.
+int run_schedule(const int32_t *cu, int32_t n_seg, int32_t total_tokens, int32_t block_rows,
+                 hipStream_t stream, int32_t **ws_out, ScheduleLayout *lay_out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
+    int32_t *err = nullptr;
+    int rc = error_word(dev, &err);
+    if (rc) return rc;
+    const int64_t n_max = max_items(total_tokens, n_seg, block_rows);
+    const int64_t hist_len = qblocks(total_tokens, block_rows) + 2;
+    if (hist_len > INT32_MAX || n_max > INT32_MAX / 2) return KEV_ERR_INVALID_ARG;
+    const ScheduleLayout lay = schedule_layout(n_seg, (int32_t)hist_len, n_max);
+    void *ws = nullptr;
+    rc = workspace(state().sched_ws, dev, stream, (size_t)lay.total * sizeof(int32_t), &ws);
+    if (rc) return rc;
+    ScheduleArgs sa{cu, n_seg, total_tokens, block_rows, (int32_t)hist_len,
+                    static_cast<int32_t *>(ws), err};
+    rc = to_status(launch_schedule(sa, stream));
+    if (rc) return rc;
+    *ws_out = static_cast<int32_t *>(ws);
+    *lay_out = lay;
+    return KEV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kev_status_string(int status) {
+    switch (status) {
+    case KEV_OK: return "ok";
+    case KEV_ERR_INVALID_ARG: return "invalid argument";
+    case KEV_ERR_UNSUPPORTED: return "unsupported dtype/head_dim combination";
+    case KEV_ERR_BAD_SEQLENS: return "cu_seqlens must start at 0, be non-decreasing and end at total_tokens";
+    case KEV_ERR_SLOT_OVERFLOW: return "cache length outside [1, slot capacity]";
+    case KEV_ERR_BAD_SLOT: return "slot id out of range or repeated";
+    case KEV_ERR_DEVICE: return "HIP runtime error";
+    case KEV_ERR_NO_MEMORY: return "workspace allocation failed";
+    default: return "unknown status";
+    }
+}
+
+int kev_prefill_block_rows(int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype) {
+    if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0) return 0;
+    if (!prefill_supported(head_dim, dtype)) return 0;
+    return block_rows_for(heads, kv_heads, dtype);
+}
+
+int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
+                            const int32_t *cu_seqlens, int32_t n_seg,
+                            int32_t heads, int32_t kv_heads, int32_t head_dim,
+                            void *out, int32_t total_tokens, int32_t dtype, void *stream_) {
+    if (n_seg < 0 || total_tokens < 0 || heads <= 0 || kv_heads <= 0 || head_dim <= 0)
+        return KEV_ERR_INVALID_ARG;
+    if (heads % kv_heads != 0) return KEV_ERR_INVALID_ARG;
+    if (dtype != KEV_BF16 && dtype != KEV_F32) return KEV_ERR_UNSUPPORTED;
+    if (!prefill_supported(head_dim, dtype)) return KEV_ERR_UNSUPPORTED;
+    if (n_seg == 0) return total_tokens == 0 ? KEV_OK : KEV_ERR_BAD_SEQLENS;
+    if (!cu_seqlens) return KEV_ERR_INVALID_ARG;
+    if (total_tokens > 0 && (!q || !k || !v || !out)) return KEV_ERR_INVALID_ARG;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+
+    if (check_enabled()) {
+        std::vector<int32_t> h(n_seg + 1);
+        if (hipMemcpyAsync(h.data(), cu_seqlens, sizeof(int32_t) * (n_seg + 1),
+                           hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess)
+            return KEV_ERR_DEVICE;
+        int rc = host_check_seqlens(h.data(), n_seg, total_tokens);
+        if (rc) return rc;
+    }
+    const int32_t br = block_rows_for(heads, kv_heads, dtype);
+    int32_t *ws = nullptr;
+    ScheduleLayout lay;
+    int rc = run_schedule(cu_seqlens, n_seg, total_tokens, br, stream, &ws, &lay);
+    if (rc) return rc;
+    if (total_tokens == 0) return KEV_OK;   // only empty questions; cu_seqlens still checked
+
+    const int64_t n_max = max_items(total_tokens, n_seg, br);
+    PrefillArgs pa{};
+    pa.q = q;
+    pa.k = k;
+    pa.v = v;
+    pa.out = out;
+    pa.cu = cu_seqlens;
+    pa.sched = ws;
+    pa.items_off = lay.items;
+    pa.heads = heads;
+    pa.kv_heads = kv_heads;
+    pa.group = heads / kv_heads;
+    pa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    if (dtype == KEV_BF16) {
+        const PrefillShape sh = prefill_shape_bf16(heads, kv_heads);
+        pa.heads_per_wg = sh.heads_per_wg;
+        pa.row_blocks = sh.row_blocks;
+        pa.block_rows = sh.block_rows;
+        pa.n_hgroups = heads / sh.heads_per_wg;
+        const int64_t grid = n_max * pa.n_hgroups;
+        if (grid > INT32_MAX) return KEV_ERR_INVALID_ARG;
+        return to_status(launch_prefill_bf16(pa, head_dim, sh.waves, grid, stream));
+    }
+    pa.heads_per_wg = 1;
+    pa.row_blocks = 1;
+    pa.block_rows = kF32BlockRows;
+    pa.n_hgroups = heads;
+    const int64_t grid = n_max * heads;
+    if (grid > INT32_MAX) return KEV_ERR_INVALID_ARG;
+    return to_status(launch_prefill_f32(pa, head_dim, grid, stream));
+}
+
+int kev_slot_attn_decode(const void *q, const kev_kv_pool *pool, const int32_t *slot_ids,
+                         const int32_t *cache_lens, void *out, const void *k_new,
+                         const void *v_new, int32_t n_req, int32_t heads, void *stream_) {
+    if (!pool || n_req < 0 || heads <= 0) return KEV_ERR_INVALID_ARG;
+    if (pool->n_slots <= 0 || pool->capacity <= 0 || pool->kv_heads <= 0 || pool->head_dim <= 0)
+        return KEV_ERR_INVALID_ARG;
+    if (heads % pool->kv_heads != 0) return KEV_ERR_INVALID_ARG;
+    if (pool->dtype != KEV_BF16) return KEV_ERR_UNSUPPORTED;
+    if (pool->head_dim != 64 && pool->head_dim != 128) return KEV_ERR_UNSUPPORTED;
+    if (heads / pool->kv_heads > 8) return KEV_ERR_UNSUPPORTED;
+    if (n_req == 0) return KEV_OK;
+    if (n_req > pool->n_slots) return KEV_ERR_BAD_SLOT;
+    if (!q || !pool->data || !slot_ids || !cache_lens || !out || !k_new || !v_new)
+        return KEV_ERR_INVALID_ARG;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+
+    if (check_enabled()) {
+        std::vector<int32_t> ids(n_req), lens(n_req);
+        if (hipMemcpyAsync(ids.data(), slot_ids, sizeof(int32_t) * n_req, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipMemcpyAsync(lens.data(), cache_lens, sizeof(int32_t) * n_req, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess)
+            return KEV_ERR_DEVICE;
+        std::vector<char> seen(pool->n_slots, 0);
+        for (int32_t r = 0; r < n_req; ++r) {
+            if (ids[r] < 0 || ids[r] >= pool->n_slots || seen[ids[r]]) return KEV_ERR_BAD_SLOT;
+            seen[ids[r]] = 1;
+            if (lens[r] < 1 || lens[r] > pool->capacity) return KEV_ERR_SLOT_OVERFLOW;
+        }
+    }
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
+    int32_t *err = nullptr;
+    int rc = error_word(dev, &err);
+    if (rc) return rc;
+
+    DecodeArgs da{};
+    da.q = q;
+    da.pool = pool->data;
+    da.slot_ids = slot_ids;
+    da.cache_lens = cache_lens;
+    da.out = out;
+    da.k_new = k_new;
+    da.v_new = v_new;
+    da.n_req = n_req;
+    da.heads = heads;
+    da.kv_heads = pool->kv_heads;
+    da.group = heads / pool->kv_heads;
+    da.n_slots = pool->n_slots;
+    da.capacity = pool->capacity;
+    da.chunk = kDecodeChunk;
+    da.max_chunks = (pool->capacity + kDecodeChunk - 1) / kDecodeChunk;
+    da.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pool->head_dim));
+    da.err = err;
+    const int64_t units = (int64_t)n_req * pool->kv_heads;
+    if (units * da.max_chunks > INT32_MAX) return KEV_ERR_INVALID_ARG;
+    const size_t counter_bytes = ((size_t)units * sizeof(int32_t) + 255) & ~(size_t)255;
+    const size_t partial_bytes =
+        (size_t)units * da.max_chunks * da.group * (pool->head_dim + 2) * sizeof(float);
+    void *ws = nullptr;
+    rc = workspace(state().decode_ws, dev, stream, counter_bytes + partial_bytes, &ws);
+    if (rc) return rc;
+    da.counters = static_cast<int32_t *>(ws);
+    da.partials = reinterpret_cast<float *>(static_cast<char *>(ws) + counter_bytes);
+    return to_status(launch_decode_bf16(da, pool->head_dim, stream));
+}
+
+int kev_get_device_errors(void *stream_, int32_t *flags_out) {
+    if (!flags_out) return KEV_ERR_INVALID_ARG;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
+    int32_t *err = nullptr;
+    int rc = error_word(dev, &err);
+    if (rc) return rc;
+    if (hipStreamSynchronize(stream) != hipSuccess) return KEV_ERR_DEVICE;
+    int32_t v = 0;
+    if (hipMemcpy(&v, err, sizeof v, hipMemcpyDeviceToHost) != hipSuccess) return KEV_ERR_DEVICE;
+    if (hipMemset(err, 0, sizeof v) != hipSuccess) return KEV_ERR_DEVICE;
+    if (hipDeviceSynchronize() != hipSuccess) return KEV_ERR_DEVICE;
+    *flags_out = v;
+    return KEV_OK;
+}
+
+int kev_schedule_host(const int32_t *cu, int32_t n_seg, int32_t block_rows, int32_t *items_out,
+                      int32_t max_items_, int32_t *n_items_out) {
+    if (!cu || n_seg < 0 || block_rows <= 0 || !n_items_out) return KEV_ERR_INVALID_ARG;
+    if (n_seg == 0) {
+        *n_items_out = 0;
+        return KEV_OK;
+    }
+    int rc = host_check_seqlens(cu, n_seg, cu[n_seg]);
+    if (rc) return rc;
+    std::vector<int32_t> nb(n_seg), order(n_seg);
+    int32_t maxnb = 0;
+    int64_t total = 0;
+    for (int32_t s = 0; s < n_seg; ++s) {
+        nb[s] = qblocks(cu[s + 1] - cu[s], block_rows);
+        maxnb = std::max(maxnb, nb[s]);
+        total += nb[s];
+        order[s] = s;
+    }
+    if (total > max_items_ || (total > 0 && !items_out)) return KEV_ERR_INVALID_ARG;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return nb[x] > nb[y]; });
+    int64_t p = 0;
+    for (int32_t t = maxnb - 1; t >= 0; --t)
+        for (int32_t i = 0; i < n_seg && nb[order[i]] > t; ++i) {
+            items_out[2 * p] = order[i];
+            items_out[2 * p + 1] = t;
+            ++p;
+        }
+    *n_items_out = (int32_t)p;
+    return KEV_OK;
+}
+
+int kev_schedule_device(const int32_t *cu_seqlens, int32_t n_seg, int32_t total_tokens,
+                        int32_t block_rows, int32_t *items_out, int32_t max_items_,
+                        int32_t *n_items_out, void *stream_) {
+    if (!cu_seqlens || n_seg <= 0 || total_tokens < 0 || block_rows <= 0 || !n_items_out)
+        return KEV_ERR_INVALID_ARG;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    int32_t *ws = nullptr;
+    ScheduleLayout lay;
+    int rc = run_schedule(cu_seqlens, n_seg, total_tokens, block_rows, stream, &ws, &lay);
+    if (rc) return rc;
+    int32_t n = 0;
+    if (hipMemcpyAsync(&n, ws, sizeof n, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return KEV_ERR_DEVICE;
+    if (n > max_items_ || (n > 0 && !items_out)) return KEV_ERR_INVALID_ARG;
+    if (n > 0 && (hipMemcpyAsync(items_out, ws + lay.items, sizeof(int32_t) * 2 * n,
+                                 hipMemcpyDeviceToHost, stream) != hipSuccess ||
+                  hipStreamSynchronize(stream) != hipSuccess))
+        return KEV_ERR_DEVICE;
+    *n_items_out = n;
+    return KEV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// kev_internal.h -- shared declarations of the HIP library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kev {
+
+// ---------------------------------------------------------------------------
+// Work decomposition of the packed prefill (host and device use the same math).
+//
+// A question s of length L is cut into query blocks of `block_rows` rows; block
+// t covers rows [t*block_rows, min((t+1)*block_rows, L)) of the question and
+// needs keys [0, min((t+1)*block_rows, L)) of the same question: everything at
+// or left of its diagonal and nothing of any other question.  Work items are
+// (question, query block) pairs; all items of one query-block index t cost the
+// same (t+1 blocks of keys), so listing them with t descending starts the
+// longest items first.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int32_t qblocks(int32_t len, int32_t block_rows) {
+    return len <= 0 ? 0 : (len + block_rows - 1) / block_rows;
+}
+
+// Upper bound on the number of items for total_tokens tokens in n_seg questions.
+__host__ __device__ inline int64_t max_items(int64_t total_tokens, int64_t n_seg,
+                                             int32_t block_rows) {
+    return (total_tokens + block_rows - 1) / block_rows + n_seg;
+}
+
+// Rows per query block and heads per workgroup chosen for a head layout.
+struct PrefillShape {
+    int32_t heads_per_wg;   // query heads of one KV group handled together (shares K/V tiles)
+    int32_t row_blocks;     // 32-row blocks per item (one wavefront each, per head)
+    int32_t block_rows;     // 32 * row_blocks
+    int32_t waves;          // heads_per_wg * row_blocks
+};
+
+inline PrefillShape prefill_shape_bf16(int32_t heads, int32_t kv_heads) {
+    int32_t G = heads / kv_heads;
+    int32_t gw = 1;
+    for (int32_t c = 8; c >= 1; --c)
+        if (G % c == 0) { gw = c; break; }
+    int32_t r = 8 / gw;
+    if (r > 4) r = 4;
+    if (r < 1) r = 1;
+    return PrefillShape{gw, r, 32 * r, gw * r};
+}
+
+constexpr int32_t kF32BlockRows = 64;   // fp32 path: one wavefront of 64 rows per item and head
+
+// ---------------------------------------------------------------------------
+// Launch arguments
+// ---------------------------------------------------------------------------
+struct ScheduleArgs {
+    const int32_t *cu;        // [n_seg + 1]
+    int32_t n_seg;
+    int32_t total_tokens;
+    int32_t block_rows;
+    int32_t hist_len;         // >= max query blocks per question + 2
+    int32_t *ws;              // workspace, see schedule_ws_ints()
+    int32_t *err;             // device error word
+};
+
+// Workspace layout of the scheduler (int32 units):
+//   [0] n_items  [1] flags  [2..] hist[hist_len] | fill[hist_len] | cnt[hist_len] |
+//   start[hist_len] | sigma[n_seg] | items[2 * max_items]
+struct ScheduleLayout {
+    int64_t hist, fill, cnt, start, sigma, items, total;
+};
+__host__ __device__ inline ScheduleLayout schedule_layout(int32_t n_seg, int32_t hist_len, int64_t n_max_items) {
+    ScheduleLayout L;
+    L.hist = 4;
+    L.fill = L.hist + hist_len;
+    L.cnt = L.fill + hist_len;
+    L.start = L.cnt + hist_len;
+    L.sigma = L.start + hist_len;
+    L.items = (L.sigma + n_seg + 3) & ~int64_t(3);
+    L.total = L.items + 2 * n_max_items;
+    return L;
+}
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    void *out;
+    const int32_t *cu;
+    const int32_t *sched;     // scheduler workspace (n_items at [0], items at items_off)
+    int64_t items_off;
+    int32_t heads, kv_heads, group;     // group = heads / kv_heads
+    int32_t heads_per_wg, row_blocks, block_rows, n_hgroups;
+    float scale_log2;                   // log2(e) / sqrt(head_dim)
+};
+
+struct DecodeArgs {
+    const void *q;
+    void *pool;
+    const int32_t *slot_ids, *cache_lens;
+    void *out;
+    const void *k_new, *v_new;
+    int32_t n_req, heads, kv_heads, group, n_slots, capacity;
+    int32_t chunk;            // positions per workgroup
+    int32_t max_chunks;       // ceil(capacity / chunk)
+    float scale_log2;
+    float *partials;          // [n_req*kv_heads][max_chunks][group][head_dim + 2]
+    int32_t *counters;        // [n_req*kv_heads], zero between calls
+    int32_t *err;
+};
+
+// Launchers (each lives in the translation unit of its kernel).
+hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int32_t waves,
+                               int64_t grid, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs &a, int32_t head_dim, int64_t grid,
+                              hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs &a, int32_t head_dim, hipStream_t s);
+
+// Decode workgroup geometry.
+constexpr int32_t kDecodeWaves = 4;
+constexpr int32_t kDecodeChunk = 256;   // positions per workgroup (64 per wavefront)
+
+}  // namespace kev

@@ -1,0 +1,147 @@
+// kev_schedule.hip -- device work-list builder for the packed prefill.
+//
+// Replaces the dense mask: the pages build a T x T causal x block-diagonal
+// matrix (Kev article, icman.com.cn, sections 2.3 and 5.3) whose construction
+// they measure at 15-20% of inference time (section 5.4) and whose size grows
+// as T^2 (section 6.4).  Here one workgroup reads cu_seqlens and lists the
+// (question, query block) items; the attention kernel then visits only key
+// blocks inside the item's own question at or left of its diagonal, so
+// cross-question and future tiles are never loaded.
+//
+// Order: query-block index t descending (cost t+1 key blocks, so the longest
+// items are issued first); within one t, questions come in descending length
+// order, ties in an unspecified order (an atomic counting sort).  The order
+// only decides which workgroup computes what: every item is computed the same
+// way wherever it runs, so outputs do not depend on it.
+#include "kev_internal.h"
+#include "../../include/kev.h"
+
+namespace kev {
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+// Inclusive prefix sum over the workgroup; *total receives the sum of all v.
+__device__ int32_t block_scan(int32_t v, int32_t *lds, int32_t *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int32_t t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    if (lane == 63) lds[wave] = v;
+    __syncthreads();
+    if (wave == 0) {
+        int32_t w = lane < kWaves ? lds[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < kWaves; o <<= 1) {
+            int32_t t = __shfl_up(w, o);
+            if (lane >= o) w += t;
+        }
+        if (lane < kWaves) lds[lane] = w;
+    }
+    __syncthreads();
+    int32_t add = wave > 0 ? lds[wave - 1] : 0;
+    *total = lds[kWaves - 1];
+    __syncthreads();
+    return v + add;
+}
+
+__global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
+    __shared__ int32_t lds[kWaves];
+    __shared__ int32_t s_bad, s_maxnb;
+    const int tid = threadIdx.x;
+    const ScheduleLayout lay = schedule_layout(a.n_seg, a.hist_len, 0);
+    int32_t *ws = a.ws;
+    int32_t *hist = ws + lay.hist, *fill = ws + lay.fill, *cnt = ws + lay.cnt;
+    int32_t *start = ws + lay.start, *sigma = ws + lay.sigma, *items = ws + lay.items;
+    const int32_t br = a.block_rows;
+
+    for (int i = tid; i < a.hist_len; i += kThreads) {
+        hist[i] = 0;
+        fill[i] = 0;
+    }
+    if (tid == 0) {
+        s_bad = (a.cu[0] != 0 || a.cu[a.n_seg] != a.total_tokens) ? 1 : 0;
+        s_maxnb = 0;
+    }
+    __syncthreads();
+
+    // Query blocks per question and their histogram.
+    int32_t my_max = 0, bad = 0;
+    for (int s = tid; s < a.n_seg; s += kThreads) {
+        int32_t len = a.cu[s + 1] - a.cu[s];
+        int32_t nb = qblocks(len, br);
+        if (len < 0 || nb + 1 >= a.hist_len) {
+            bad = 1;
+            continue;
+        }
+        atomicAdd(&hist[nb], 1);
+        my_max = max(my_max, nb);
+    }
+    if (bad) atomicOr(&s_bad, 1);
+    atomicMax(&s_maxnb, my_max);
+    __syncthreads();
+    if (s_bad) {
+        if (tid == 0) {
+            ws[0] = 0;
+            atomicOr(a.err, (int32_t)KEV_DEVERR_SEQLENS);
+        }
+        return;
+    }
+    const int32_t maxnb = s_maxnb;
+
+    // cnt[c] = #questions with more than c query blocks = sum of hist[c+1 .. maxnb].
+    int32_t carry = 0, tot;
+    for (int base = 0; base < maxnb; base += kThreads) {
+        int j = base + tid;
+        int32_t x = j < maxnb ? hist[maxnb - j] : 0;
+        int32_t incl = block_scan(x, lds, &tot) + carry;
+        if (j < maxnb) cnt[maxnb - 1 - j] = incl;
+        carry += tot;
+    }
+    if (tid == 0) cnt[maxnb] = 0;
+    __syncthreads();
+
+    // start[e] = first position of level e (query block t = maxnb-1-e).
+    carry = 0;
+    for (int base = 0; base < maxnb; base += kThreads) {
+        int j = base + tid;
+        int32_t y = j < maxnb ? cnt[maxnb - 1 - j] : 0;
+        int32_t incl = block_scan(y, lds, &tot) + carry;
+        if (j < maxnb) start[j] = incl - y;
+        carry += tot;
+    }
+    const int32_t n_items = carry;
+
+    // sigma: questions in descending block count.
+    for (int s = tid; s < a.n_seg; s += kThreads) {
+        int32_t nb = qblocks(a.cu[s + 1] - a.cu[s], br);
+        if (nb > 0) sigma[cnt[nb] + atomicAdd(&fill[nb], 1)] = s;
+    }
+    __syncthreads();
+
+    // At level t the questions with more than t blocks are sigma[0 .. cnt[t]).
+    for (int p = tid; p < n_items; p += kThreads) {
+        int lo = 0, hi = maxnb - 1;
+        while (lo < hi) {
+            int mid = (lo + hi + 1) >> 1;
+            if (start[mid] <= p) lo = mid;
+            else hi = mid - 1;
+        }
+        items[2 * p] = sigma[p - start[lo]];
+        items[2 * p + 1] = maxnb - 1 - lo;
+    }
+    if (tid == 0) ws[0] = n_items;
+}
+
+}  // namespace
+
+hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace kev

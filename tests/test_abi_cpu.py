@@ -1,0 +1,134 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, rejects bad
+arguments before touching the GPU, and its host-side tile math covers every unmasked
+(query, key) pair of every question exactly once."""
+import ctypes
+import re
+
+import numpy as np
+import pytest
+
+import segment_isolated_packed_amd as K
+from segment_isolated_packed_amd import workloads as W
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return K.load_library()
+
+
+def declared_functions():
+    text = open(K.HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kev_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"kev_packed_attn_prefill", "kev_slot_attn_decode", "kev_status_string",
+            "kev_get_device_errors"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(0, -8, -1):
+        assert K.status_string(code) not in ("", "unknown status")
+    assert K.status_string(42) == "unknown status"
+
+
+def _prefill(lib, n_seg=1, heads=4, kv_heads=4, d=128, T=10, dtype=0, cu=True):
+    p = ctypes.c_void_p(16) if cu else None
+    return lib.kev_packed_attn_prefill(p, p, p, p, n_seg, heads, kv_heads, d, p, T, dtype, None)
+
+
+def test_prefill_argument_checks(lib):
+    assert _prefill(lib, heads=6, kv_heads=4) == K.KEV_ERR_INVALID_ARG
+    assert _prefill(lib, heads=0) == K.KEV_ERR_INVALID_ARG
+    assert _prefill(lib, n_seg=-1) == K.KEV_ERR_INVALID_ARG
+    assert _prefill(lib, T=-5) == K.KEV_ERR_INVALID_ARG
+    assert _prefill(lib, d=96) == K.KEV_ERR_UNSUPPORTED
+    assert _prefill(lib, d=16, dtype=0) == K.KEV_ERR_UNSUPPORTED
+    assert _prefill(lib, d=256, dtype=1) == K.KEV_ERR_UNSUPPORTED
+    assert _prefill(lib, dtype=7) == K.KEV_ERR_UNSUPPORTED
+    assert _prefill(lib, cu=False) == K.KEV_ERR_INVALID_ARG
+    assert _prefill(lib, n_seg=0, T=0) == K.KEV_OK          # no-op, no HIP call
+    assert _prefill(lib, n_seg=0, T=3) == K.KEV_ERR_BAD_SEQLENS
+
+
+def _decode(lib, n_req=4, heads=32, n_slots=8, cap=64, kvh=8, d=128, dtype=0, null=False):
+    pool = K.KvPool(16, n_slots, cap, kvh, d, dtype)
+    p = None if null else ctypes.c_void_p(16)
+    return lib.kev_slot_attn_decode(p, ctypes.byref(pool), p, p, p, p, p, n_req, heads, None)
+
+
+def test_decode_argument_checks(lib):
+    assert _decode(lib, heads=30) == K.KEV_ERR_INVALID_ARG
+    assert _decode(lib, n_slots=0) == K.KEV_ERR_INVALID_ARG
+    assert _decode(lib, cap=0) == K.KEV_ERR_INVALID_ARG
+    assert _decode(lib, dtype=1) == K.KEV_ERR_UNSUPPORTED
+    assert _decode(lib, d=96) == K.KEV_ERR_UNSUPPORTED
+    assert _decode(lib, heads=72, kvh=4) == K.KEV_ERR_UNSUPPORTED      # group of 18
+    assert _decode(lib, n_req=9) == K.KEV_ERR_BAD_SLOT                  # more requests than slots
+    assert _decode(lib, null=True) == K.KEV_ERR_INVALID_ARG
+    assert _decode(lib, n_req=0) == K.KEV_OK
+    assert lib.kev_slot_attn_decode(None, None, None, None, None, None, None, 1, 4, None) \
+        == K.KEV_ERR_INVALID_ARG
+
+
+def test_block_rows(lib):
+    assert K.kev_prefill_block_rows(28, 4, 128, K.KEV_BF16) == 32     # 7 heads x 1 row block
+    assert K.kev_prefill_block_rows(32, 8, 128, K.KEV_BF16) == 64     # 4 heads x 2 row blocks
+    assert K.kev_prefill_block_rows(4, 4, 128, K.KEV_BF16) == 128     # MHA: 4 row blocks
+    assert K.kev_prefill_block_rows(4, 4, 16, K.KEV_F32) == 64
+    assert K.kev_prefill_block_rows(4, 3, 128, K.KEV_BF16) == 0
+
+
+def covered_pairs(items, cu, block_rows):
+    """(row, key) pairs the attention kernel evaluates unmasked, per question.
+
+    Mirrors the kernel's visiting rule: a wavefront owns 32 rows of an item and
+    visits 32-key sub-blocks that start before min(its last row + 1, L); inside a
+    sub-block, keys past the row or past the question are masked."""
+    seen = {}
+    for s, t in items:
+        a, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        for rb in range(block_rows // 32):
+            row0 = t * block_rows + rb * 32
+            if row0 >= L:
+                continue
+            key_end = min(row0 + 32, L)
+            for ks in range(0, key_end, 32):
+                for i in range(row0, min(row0 + 32, L)):
+                    for j in range(ks, min(ks + 32, L)):
+                        if j <= i:
+                            seen[(a + i, a + j)] = seen.get((a + i, a + j), 0) + 1
+    return seen
+
+
+@pytest.mark.parametrize("block_rows", [32, 64, 128])
+def test_schedule_covers_each_unmasked_pair_once(block_rows):
+    rng = np.random.default_rng(block_rows)
+    for trial in range(4):
+        lens = rng.integers(0, 300, size=int(rng.integers(1, 9)))
+        lens[0] = max(lens[0], 1)
+        cu = W.cu_from_lengths(lens)
+        items = K.kev_schedule_host(cu, block_rows)
+        assert len(items) == sum(-(-int(x) // block_rows) for x in lens)
+        assert len({(int(s), int(t)) for s, t in items}) == len(items)
+        # heaviest first: query-block index never increases along the list
+        assert (np.diff(items[:, 1]) <= 0).all()
+        seen = covered_pairs(items, cu, block_rows)
+        expect = {(int(cu[s]) + i, int(cu[s]) + j) for s in range(len(lens))
+                  for i in range(int(lens[s])) for j in range(i + 1)}
+        assert set(seen) == expect
+        assert all(c == 1 for c in seen.values())
+
+
+def test_skewed_long_visits_a_small_fraction_of_global_causal_tiles():
+    lens = W.prefill_lengths("skewed_long")
+    cu = W.cu_from_lengths(lens)
+    items = K.kev_schedule_host(cu, 64)
+    tiles = int(sum(-(-min((int(t) + 1) * 64, int(lens[s])) // 64) for s, t in items))
+    T = int(cu[-1])
+    n = T // 64
+    global_causal = n * (n + 1) // 2
+    assert tiles / global_causal < 0.04
