@@ -82,8 +82,9 @@ def main():
                     choices=["qwen25_7b", "qwen3_8b", "skewed_long"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="run one half of the step (profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="run one half of the step, or a 1 GiB device copy that calibrates "
+                         "the HBM byte counters (profiling runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -105,22 +106,33 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    log(f"generating {args.workload} prefill inputs")
-    pc = W.prefill_case(args.workload)
-    q, k, v = (to_dev(x, pc.dtype) for x in (pc.q, pc.k, pc.v))
-    cu = torch.from_numpy(pc.cu_seqlens).to(dev)
-    out = torch.empty_like(q)
-    log("generating slot-decode inputs")
-    dc = W.make_decode()
-    dq, dpool, dkn, dvn = (to_dev(x, dc.dtype) for x in (dc.q, dc.pool, dc.k_new, dc.v_new))
-    dids = torch.from_numpy(dc.slot_ids).to(dev)
-    dlens = torch.from_numpy(dc.cache_lens).to(dev)
-    dout = torch.empty_like(dq)
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
+    if args.only == "copy":
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": 2 * src.numel(), "launches": args.warmup + args.steps}))
+        return
 
     do_pre = args.only in (None, "prefill")
     do_dec = args.only in (None, "decode")
+    pc = dc = None
+    if do_pre:
+        log(f"generating {args.workload} prefill inputs")
+        pc = W.prefill_case(args.workload)
+        q, k, v = (to_dev(x, pc.dtype) for x in (pc.q, pc.k, pc.v))
+        cu = torch.from_numpy(pc.cu_seqlens).to(dev)
+        out = torch.empty_like(q)
+    if do_dec:
+        log("generating slot-decode inputs")
+        dc = W.make_decode()
+        dq, dpool, dkn, dvn = (to_dev(x, dc.dtype) for x in (dc.q, dc.pool, dc.k_new, dc.v_new))
+        dids = torch.from_numpy(dc.slot_ids).to(dev)
+        dlens = torch.from_numpy(dc.cache_lens).to(dev)
+        dout = torch.empty_like(dq)
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
 
     def step(ev=None):
         if do_pre:
@@ -156,8 +168,8 @@ def main():
     dec_ms = [e[2].elapsed_time(e[3]) for e in events] if do_dec else [float("nan")]
     pre_avg = float(np.mean(pre_ms))
     dec_avg = float(np.mean(dec_ms))
-    flops = pc.effective_flops()
-    dbytes = dc.algorithmic_bytes()
+    flops = pc.effective_flops() if do_pre else 0
+    dbytes = dc.algorithmic_bytes() if do_dec else 0
     tflops = flops / (pre_avg * 1e-3) / 1e12 if do_pre else None
     gbps = dbytes / (dec_avg * 1e-3) / 1e9 if do_dec else None
 
@@ -179,11 +191,11 @@ def main():
         "config": {
             "workload": f"{args.workload} packed prefill + slot-pool decode",
             "prefill": W.PREFILL_DESCRIPTIONS[args.workload],
-            "prefill_seed": pc.seed,
-            "prefill_tokens": pc.total_tokens,
+            "prefill_seed": pc.seed if pc else None,
+            "prefill_tokens": pc.total_tokens if pc else None,
             "prefill_effective_gflop": flops / 1e9,
             "decode": W.DECODE_DESCRIPTION,
-            "decode_seed": dc.seed,
+            "decode_seed": dc.seed if dc else None,
             "decode_algorithmic_mb": dbytes / 1e6,
             "step": "prefill call (scheduler + attention kernel), 512 MiB flush write, decode call",
         },
@@ -205,7 +217,7 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and do_pre:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(pc)
     print(json.dumps(result), flush=True)

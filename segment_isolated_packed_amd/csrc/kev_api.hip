@@ -35,7 +35,7 @@ struct State {
     std::mutex mu;
     std::map<int, int32_t *> err_word;                        // device -> error word
     std::map<std::pair<int, void *>, Buffer> sched_ws;        // (device, stream)
-    std::map<std::pair<int, void *>, Buffer> decode_ws;       // (device, stream), zeroed counters
+    std::map<std::pair<int, void *>, Buffer> decode_ws;       // (device, stream)
 };
 
 State &state() {
@@ -67,9 +67,7 @@ int error_word(int dev, int32_t **out) {
     return KEV_OK;
 }
 
-// Workspace of at least `bytes` for (device, stream).  Grown buffers are zeroed
-// on the stream before first use; decode relies on its counters starting at 0
-// and returns them to 0 itself.
+// Workspace of at least `bytes` for (device, stream), grown on demand.
 int workspace(std::map<std::pair<int, void *>, Buffer> &m, int dev, hipStream_t stream,
               size_t bytes, void **out) {
     State &st = state();
@@ -87,7 +85,6 @@ int workspace(std::map<std::pair<int, void *>, Buffer> &m, int dev, hipStream_t 
             b.ptr = nullptr;
             return KEV_ERR_NO_MEMORY;
         }
-        if (hipMemsetAsync(b.ptr, 0, want, stream) != hipSuccess) return KEV_ERR_DEVICE;
         b.bytes = want;
     }
     *out = b.ptr;
@@ -278,14 +275,12 @@ int kev_slot_attn_decode(const void *q, const kev_kv_pool *pool, const int32_t *
     da.err = err;
     const int64_t units = (int64_t)n_req * pool->kv_heads;
     if (units * da.max_chunks > INT32_MAX) return KEV_ERR_INVALID_ARG;
-    const size_t counter_bytes = ((size_t)units * sizeof(int32_t) + 255) & ~(size_t)255;
     const size_t partial_bytes =
         (size_t)units * da.max_chunks * da.group * (pool->head_dim + 2) * sizeof(float);
     void *ws = nullptr;
-    rc = workspace(state().decode_ws, dev, stream, counter_bytes + partial_bytes, &ws);
+    rc = workspace(state().decode_ws, dev, stream, partial_bytes, &ws);
     if (rc) return rc;
-    da.counters = static_cast<int32_t *>(ws);
-    da.partials = reinterpret_cast<float *>(static_cast<char *>(ws) + counter_bytes);
+    da.partials = static_cast<float *>(ws);
     return to_status(launch_decode_bf16(da, pool->head_dim, stream));
 }
 

@@ -20,8 +20,12 @@
 //     rows (scores via v_dot2_f32_bf16, cross-lane sums via DPP);
 //   - the softmax is blockwise online (running max / sum / rescaled
 //     accumulator, primer section 2.4) over 32-position sub-blocks, then
-//     wavefronts are merged in LDS and chunks are merged by the last
-//     workgroup of the unit to finish, with the same rescaling identity.
+//     wavefronts are merged in LDS; a unit with one chunk writes its output
+//     directly, otherwise each chunk writes (max, sum, accumulator) and a
+//     second small kernel merges the chunks with the same rescaling identity.
+//     (A last-arriving-workgroup merge inside one kernel would need
+//     device-scope fences, which write back and invalidate the XCD's L2 on
+//     every workgroup; the kernel boundary gives the same ordering once.)
 #include "kev_internal.h"
 #include "../../include/kev.h"
 
@@ -77,9 +81,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(DecodeAr
     constexpr int NI = SB / RPI;       // instructions per sub-block
     __shared__ float w_m[NW][GMAX], w_l[NW][GMAX];
     __shared__ float w_acc[NW][GMAX][D];
-    __shared__ int s_last;
 
-    const int G = p.group;
+    const int G = (GMAX == 1 || GMAX == 2 || GMAX == 4) ? GMAX : p.group;
     const int unit = blockIdx.x / p.max_chunks;
     const int c = blockIdx.x % p.max_chunks;
     const int r = unit / p.kv_heads, g = unit % p.kv_heads;
@@ -243,23 +246,25 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(DecodeAr
             }
         }
     }
-    if (nchunks == 1) return;
+}
 
-    // The last workgroup of the unit to finish merges the chunks.
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        int prev = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == nchunks - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int e = tid; e < G * D; e += NW * 64) {
+// Merge the chunk partials of every unit that spans more than one chunk.
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs p) {
+    const int unit = blockIdx.x;
+    const int r = unit / p.kv_heads, g = unit % p.kv_heads;
+    const int slot = p.slot_ids[r];
+    const int L = p.cache_lens[r];
+    if (slot < 0 || slot >= p.n_slots || L < 1 || L > p.capacity) return;
+    const int nchunks = (L + p.chunk - 1) / p.chunk;
+    if (nchunks == 1) return;
+    const int G = p.group;
+    const float *part = p.partials + ((int64_t)unit * p.max_chunks) * G * (D + 2);
+    uint16_t *out = static_cast<uint16_t *>(p.out) + ((int64_t)r * p.heads + g * G) * D;
+    for (int e = threadIdx.x; e < G * D; e += 256) {
         const int h = e / D, d = e % D;
         float M = -INFINITY;
-        for (int cc = 0; cc < nchunks; ++cc)
-            M = fmaxf(M, part[((int64_t)cc * G + h) * (D + 2) + D]);
+        for (int cc = 0; cc < nchunks; ++cc) M = fmaxf(M, part[((int64_t)cc * G + h) * (D + 2) + D]);
         float A = 0.f, S = 0.f;
         for (int cc = 0; cc < nchunks; ++cc) {
             const float *pp = part + ((int64_t)cc * G + h) * (D + 2);
@@ -269,23 +274,28 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(DecodeAr
         }
         out[h * D + d] = to_bf16(A / S);
     }
-    if (tid == 0) p.counters[unit] = 0;
 }
 
 template <int D, int GMAX>
 hipError_t launch(const DecodeArgs &a, hipStream_t s) {
-    const int64_t grid = (int64_t)a.n_req * a.kv_heads * a.max_chunks;
-    hipLaunchKernelGGL((decode_bf16_kernel<D, GMAX>), dim3((unsigned)grid), dim3(kDecodeWaves * 64), 0, s, a);
+    const int64_t units = (int64_t)a.n_req * a.kv_heads;
+    hipLaunchKernelGGL((decode_bf16_kernel<D, GMAX>), dim3((unsigned)(units * a.max_chunks)),
+                       dim3(kDecodeWaves * 64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.max_chunks == 1) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)units), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
-    if (a.group <= 1) return launch<D, 1>(a, s);
-    if (a.group <= 2) return launch<D, 2>(a, s);
-    if (a.group <= 4) return launch<D, 4>(a, s);
-    if (a.group <= 8) return launch<D, 8>(a, s);
-    return hipErrorInvalidValue;
+    switch (a.group) {
+    case 1: return launch<D, 1>(a, s);
+    case 2: return launch<D, 2>(a, s);
+    case 4: return launch<D, 4>(a, s);
+    case 8: return launch<D, 8>(a, s);
+    default: return launch<D, 8>(a, s);   // other group sizes up to 8, guarded by p.group
+    }
 }
 
 }  // namespace

@@ -57,7 +57,7 @@ struct ScheduleArgs {
     int32_t total_tokens;
     int32_t block_rows;
     int32_t hist_len;         // >= max query blocks per question + 2
-    int32_t *ws;              // workspace, see schedule_ws_ints()
+    int32_t *ws;              // workspace, see schedule_layout()
     int32_t *err;             // device error word
 };
 
@@ -101,7 +101,6 @@ struct DecodeArgs {
     int32_t max_chunks;       // ceil(capacity / chunk)
     float scale_log2;
     float *partials;          // [n_req*kv_heads][max_chunks][group][head_dim + 2]
-    int32_t *counters;        // [n_req*kv_heads], zero between calls
     int32_t *err;
 };
 

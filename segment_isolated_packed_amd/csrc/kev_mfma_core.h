@@ -1,0 +1,180 @@
+// kev_mfma_core.h -- gfx950 building blocks shared by the prefill and decode kernels.
+//
+// One wavefront computes, for up to 32 query rows (the B-operand columns),
+//     S^T[key][q]  = K[key][:] . Q[q][:]          (v_mfma_f32_32x32x16_bf16)
+//     O^T[d][q]   += V^T[d][key] . P^T[key][q]
+// with K and V tiles staged in LDS in their natural row-major [key][d] layout.
+//
+// Staging: global_load_lds_dwordx4 writes 64 lanes x 16 B straight into LDS
+// (no VGPR round trip).  A row of D bf16 is D/8 16-byte chunks; chunk c of row
+// r is stored at position c ^ swz(r) so that both read patterns below hit
+// distinct LDS banks.  Since a direct load writes lane i to base + 16*i, each
+// lane fetches the global chunk that belongs at its LDS position.
+//
+// Reads:
+//   K (A operand of S^T): lane l reads 16 B of row l%32 -> one ds_read_b128.
+//   V^T (A operand of O^T): ds_read_b64_tr_b16 -- within a 16-lane group,
+//   destination lane 4a+b receives element b of the 8-byte rows addressed by
+//   lanes a, a+4, a+8, a+12 -- turns four key rows x 16 d into 16 lanes of
+//   (one d, four keys); two such reads give the 8 keys of an MFMA k-slice.
+//   The key order of those 8 slots matches the rows of the S^T accumulator a
+//   lane holds (rows 8*(i/4) + 4*(lane/32) + i%4), so P^T goes from the first
+//   MFMA's accumulators to the second MFMA's B operand without leaving the lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kev {
+namespace core {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(1))) const void gbl_void;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+struct Geom {
+    static constexpr int CPR = D / 8;       // 16-byte chunks per row
+    static constexpr int RPI = 64 / CPR;    // rows per 1 KB direct-load instruction
+    static constexpr int ROWB = D * 2;      // bytes per row
+    // Chunk swizzle: 16 consecutive rows at one chunk (K reads) and 4 consecutive rows
+    // x 4 aligned chunks (transpose reads) both land on distinct 16-byte bank groups.
+    __device__ static int swz(int r) {
+        return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((r >> 1) & 7);
+    }
+    __device__ static int off(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
+};
+
+// s_waitcnt vmcnt(N) only (gfx9 encoding; expcnt / lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that the compiler may not move memory operations across.
+__device__ __forceinline__ void barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// 64 lanes x 16 B from global straight into LDS at lds_base + 16*lane
+// (global_load_lds_dwordx4; the LDS base goes through m0).  Issued as inline asm so
+// the compiler does not add its own conservative vmcnt waits before LDS reads: the
+// callers wait for these loads explicitly (wait_vmcnt + barrier) before reading the
+// stage they fill, and never read a stage that has loads in flight.
+__device__ __forceinline__ void dma16(const void *g, const lds_t *lds_base) {
+    const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(m0v)
+                 : "memory");
+}
+
+// Per-lane part of a direct load of tile rows [r0, r0 + RPI): the row this lane fills and
+// the global chunk that belongs at its LDS position (chunk c ^ swz(r) of the row).
+template <int D>
+struct DmaLane {
+    int row;     // tile row (key offset inside the tile)
+    int coff;    // element offset of the chunk inside the row
+    __device__ void init(int r0) {
+        using G = Geom<D>;
+        const int lane = threadIdx.x & 63;
+        row = r0 + lane / G::CPR;
+        coff = ((lane % G::CPR) ^ G::swz(row)) * 8;
+    }
+};
+
+// S^T for both 32-key halves of a staged K tile (two independent MFMA chains, interleaved).
+template <int D>
+__device__ __forceinline__ void scores2(const lds_t *ktile, const bf16x8 *qf, f32x16 &s0, f32x16 &s1) {
+    using G = Geom<D>;
+    const int lane = threadIdx.x & 63;
+    const int row = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        s0[i] = 0.f;
+        s1[i] = 0.f;
+    }
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+        const int off = G::off(row, 2 * dc + half);
+        const u32x4 a0 = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(ktile + off);
+        const u32x4 a1 = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(ktile + off + 32 * G::ROWB);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), qf[dc], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), qf[dc], s1, 0, 0, 0);
+    }
+}
+
+// S^T for the 32 keys [kb*32, kb*32+32) of a staged K tile against the wave's query columns.
+template <int D>
+__device__ __forceinline__ f32x16 scores(const lds_t *ktile, int kb, const bf16x8 *qf) {
+    using G = Geom<D>;
+    const int lane = threadIdx.x & 63;
+    const int row = kb * 32 + (lane & 31), half = lane >> 5;
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+        const u32x4 u = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
+            ktile + G::off(row, 2 * dc + half));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), qf[dc], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// V^T fragment (A operand) for d-block db and 16-key chunk c of a staged V tile.
+template <int D>
+__device__ __forceinline__ bf16x8 vt_frag(const lds_t *vtile, int c, int db) {
+    using G = Geom<D>;
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4, s = lane & 15;
+    const int d = db * 32 + (grp & 1) * 16 + 4 * (s & 3);
+    const int row = c * 16 + (grp >> 1) * 4 + (s >> 2);
+    const int inb = (d & 7) * 2;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)(vtile + G::off(row, d >> 3) + inb));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)(vtile + G::off(row + 8, d >> 3) + inb));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Max / sum over lanes l and l^32 (every lane gets the value for its pair).  ds_bpermute;
+// the gfx950 v_permlane32_swap builtin is not used: in this compiler its second result
+// is read from the wrong register.
+__device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Sum of the 8 bf16 values of a P^T fragment (v_dot2_f32_bf16 against ones): the row sum
+// then counts exactly the rounded weights the PV MFMA uses.
+__device__ __forceinline__ float sum8(bf16x8 p, float acc) {
+    const u32x4 w = __builtin_bit_cast(u32x4, p);
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]), one, acc, false);
+    return acc;
+}
+
+// Online-softmax state of one lane (one query column; the lane pair l, l^32 shares it).
+// The running max is only moved (and O^T, l rescaled) when a new score exceeds it by more
+// than kLazy (log2 units); otherwise weights are taken against the stale max, so they stay
+// below 2^kLazy.  Either way out = O / l is the same softmax average.
+constexpr float kLazy = 8.0f;
+
+}  // namespace core
+}  // namespace kev

@@ -49,19 +49,27 @@ __device__ int32_t block_scan(int32_t v, int32_t *lds, int32_t *total) {
     return v + add;
 }
 
+// Tables live in LDS when they fit (the common case: a few hundred questions
+// and query blocks), else in the global workspace; the code is the same through
+// generic pointers.
+constexpr int kLds = 2048;
+
 __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     __shared__ int32_t lds[kWaves];
     __shared__ int32_t s_bad, s_maxnb;
+    __shared__ int32_t t_cu[kLds + 1], t_hist[kLds], t_fill[kLds], t_cnt[kLds], t_start[kLds],
+        t_sigma[kLds];
     const int tid = threadIdx.x;
     const ScheduleLayout lay = schedule_layout(a.n_seg, a.hist_len, 0);
     int32_t *ws = a.ws;
-    int32_t *hist = ws + lay.hist, *fill = ws + lay.fill, *cnt = ws + lay.cnt;
-    int32_t *start = ws + lay.start, *sigma = ws + lay.sigma, *items = ws + lay.items;
+    int32_t *items = ws + lay.items;
     const int32_t br = a.block_rows;
+    const bool cu_small = a.n_seg + 1 <= kLds + 1;
 
-    for (int i = tid; i < a.hist_len; i += kThreads) {
-        hist[i] = 0;
-        fill[i] = 0;
+    const int32_t *cu = a.cu;
+    if (cu_small) {
+        for (int i = tid; i <= a.n_seg; i += kThreads) t_cu[i] = a.cu[i];
+        cu = t_cu;
     }
     if (tid == 0) {
         s_bad = (a.cu[0] != 0 || a.cu[a.n_seg] != a.total_tokens) ? 1 : 0;
@@ -69,17 +77,13 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     }
     __syncthreads();
 
-    // Query blocks per question and their histogram.
+    // Query blocks per question: validity and the largest count.
     int32_t my_max = 0, bad = 0;
     for (int s = tid; s < a.n_seg; s += kThreads) {
-        int32_t len = a.cu[s + 1] - a.cu[s];
+        int32_t len = cu[s + 1] - cu[s];
         int32_t nb = qblocks(len, br);
-        if (len < 0 || nb + 1 >= a.hist_len) {
-            bad = 1;
-            continue;
-        }
-        atomicAdd(&hist[nb], 1);
-        my_max = max(my_max, nb);
+        if (len < 0 || nb + 1 >= a.hist_len) bad = 1;
+        else my_max = max(my_max, nb);
     }
     if (bad) atomicOr(&s_bad, 1);
     atomicMax(&s_maxnb, my_max);
@@ -92,6 +96,20 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
         return;
     }
     const int32_t maxnb = s_maxnb;
+    const bool small = maxnb + 2 <= kLds && a.n_seg <= kLds;
+    int32_t *hist = small ? t_hist : ws + lay.hist;
+    int32_t *fill = small ? t_fill : ws + lay.fill;
+    int32_t *cnt = small ? t_cnt : ws + lay.cnt;
+    int32_t *start = small ? t_start : ws + lay.start;
+    int32_t *sigma = small ? t_sigma : ws + lay.sigma;
+
+    for (int i = tid; i < maxnb + 2; i += kThreads) {
+        hist[i] = 0;
+        fill[i] = 0;
+    }
+    __syncthreads();
+    for (int s = tid; s < a.n_seg; s += kThreads) atomicAdd(&hist[qblocks(cu[s + 1] - cu[s], br)], 1);
+    __syncthreads();
 
     // cnt[c] = #questions with more than c query blocks = sum of hist[c+1 .. maxnb].
     int32_t carry = 0, tot;
@@ -118,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
 
     // sigma: questions in descending block count.
     for (int s = tid; s < a.n_seg; s += kThreads) {
-        int32_t nb = qblocks(a.cu[s + 1] - a.cu[s], br);
+        int32_t nb = qblocks(cu[s + 1] - cu[s], br);
         if (nb > 0) sigma[cnt[nb] + atomicAdd(&fill[nb], 1)] = s;
     }
     __syncthreads();
