@@ -4,7 +4,7 @@ One step = one packed prefill over the Qwen2.5-7B-shaped workload (bf16, 28 q / 
 heads, head_dim 128, 8 questions with lengths uniform in [256, 2048], seed 42) followed
 by one slot-pool decode (bf16, 32 q / 8 kv heads, 64 requests, slot capacity 2458,
 80-slot pool, new K/V appended in-kernel, seed 44).  Between the two a 512 MiB buffer is
-written so the decode reads its KV rows from HBM rather than from the 256 MB MALL.
+read so the decode reads its KV rows from HBM rather than from the 256 MB MALL.
 
 Prints ONE JSON line.  `value` is the prefill's effective TFLOP/s (only unmasked score
 entries counted: 4 * d * heads * sum L(L+1)/2 FLOPs per call) over the average duration
@@ -81,7 +81,9 @@ def main():
     ap.add_argument("--workload", default="qwen25_7b",
                     choices=["qwen25_7b", "qwen3_8b", "skewed_long"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
+                    help="how the 256 MB MALL is evicted before each decode: read a 512 MiB "
+                         "buffer (default), write it, or not at all")
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="run one half of the step, or a 1 GiB device copy that calibrates "
                          "the HBM byte counters (profiling runs)")
@@ -131,7 +133,9 @@ def main():
         dids = torch.from_numpy(dc.slot_ids).to(dev)
         dlens = torch.from_numpy(dc.cache_lens).to(dev)
         dout = torch.empty_like(dq)
-        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        flush_buf = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        flush_rows = flush_buf.view(512, 1 << 20)
+        flush_sink = torch.zeros(512, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -140,7 +144,9 @@ def main():
             K.kev_packed_attn_prefill(q, k, v, cu, out=out)
             if ev: ev[1].record(stream)
         if do_dec:
-            if not args.no_flush:
+            if args.flush == "read":
+                torch.sum(flush_rows, dim=1, dtype=torch.int32, out=flush_sink)
+            elif args.flush == "write":
                 flush_buf.fill_(1)
             if ev: ev[2].record(stream)
             K.kev_slot_attn_decode(dq, dpool, dids, dlens, dkn, dvn, out=dout)
@@ -197,7 +203,7 @@ def main():
             "decode": W.DECODE_DESCRIPTION,
             "decode_seed": dc.seed if dc else None,
             "decode_algorithmic_mb": dbytes / 1e6,
-            "step": "prefill call (scheduler + attention kernel), 512 MiB flush write, decode call",
+            "step": f"prefill call (scheduler + attention kernel), 512 MiB MALL flush ({args.flush}), decode call",
         },
         "prefill_ms": pre_avg,
         "prefill_pct_peak": tflops / PEAK_BF16_TFLOPS * 100 if tflops else None,

@@ -228,7 +228,7 @@ int kev_slot_attn_decode(const void *q, const kev_kv_pool *pool, const int32_t *
     if (heads % pool->kv_heads != 0) return KEV_ERR_INVALID_ARG;
     if (pool->dtype != KEV_BF16) return KEV_ERR_UNSUPPORTED;
     if (pool->head_dim != 64 && pool->head_dim != 128) return KEV_ERR_UNSUPPORTED;
-    if (heads / pool->kv_heads > 8) return KEV_ERR_UNSUPPORTED;
+    if (heads / pool->kv_heads > 32) return KEV_ERR_UNSUPPORTED;   // query heads per KV head = MFMA columns
     if (n_req == 0) return KEV_OK;
     if (n_req > pool->n_slots) return KEV_ERR_BAD_SLOT;
     if (!q || !pool->data || !slot_ids || !cache_lens || !out || !k_new || !v_new)
@@ -270,7 +270,8 @@ int kev_slot_attn_decode(const void *q, const kev_kv_pool *pool, const int32_t *
     da.n_slots = pool->n_slots;
     da.capacity = pool->capacity;
     da.chunk = kDecodeChunk;
-    da.max_chunks = (pool->capacity + kDecodeChunk - 1) / kDecodeChunk;
+    while ((pool->capacity + da.chunk - 1) / da.chunk > kDecodeMaxChunks) da.chunk *= 2;
+    da.max_chunks = (pool->capacity + da.chunk - 1) / da.chunk;
     da.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pool->head_dim));
     da.err = err;
     const int64_t units = (int64_t)n_req * pool->kv_heads;

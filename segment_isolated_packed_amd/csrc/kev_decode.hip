@@ -8,93 +8,85 @@
 // slot with no mask (same section: the new query is last, so every cached
 // position is visible).  Nothing outside rows 0..L-1 of slot s is read.
 //
-// Decode reads every cached K/V byte once and does ~4 FLOP per byte, far
-// below the MI355X ridge point, so the kernel is shaped for HBM bandwidth:
+// Decode reads every cached K/V byte once; the arithmetic per byte is tiny, so
+// the kernel is shaped for HBM bandwidth and keeps the vector ALUs nearly idle:
 //   - a unit is (request, KV head); its positions are cut into chunks of
-//     kDecodeChunk positions, one workgroup per chunk, so long and short
-//     slots spread evenly over the CUs;
-//   - each wavefront streams a contiguous quarter of the chunk; 16 lanes read
-//     one 256-byte K (or V) row with 16-byte loads, 4 rows per instruction,
-//     fully coalesced along the slot's contiguous [position][d] plane;
-//   - all `group` query heads of the KV head are served from the same loaded
-//     rows (scores via v_dot2_f32_bf16, cross-lane sums via DPP);
-//   - the softmax is blockwise online (running max / sum / rescaled
-//     accumulator, primer section 2.4) over 32-position sub-blocks, then
-//     wavefronts are merged in LDS; a unit with one chunk writes its output
-//     directly, otherwise each chunk writes (max, sum, accumulator) and a
-//     second small kernel merges the chunks with the same rescaling identity.
-//     (A last-arriving-workgroup merge inside one kernel would need
-//     device-scope fences, which write back and invalidate the XCD's L2 on
-//     every workgroup; the kernel boundary gives the same ordering once.)
+//     kDecodeChunk positions, one single-wavefront workgroup per chunk, so long
+//     and short slots spread evenly over the CUs and several workgroups share
+//     a CU;
+//   - the `group` query heads of the KV head are the columns of MFMA tiles
+//     (v_mfma_f32_32x32x16_bf16: S^T = K Q^T, O^T += V^T P^T), so the dot
+//     products and the weighted sum of V cost matrix-core cycles, not VALU;
+//   - K and V rows of the slot plane go straight from HBM into LDS with direct
+//     loads, three 32-position stages deep, 1 KB per load instruction; the row
+//     holding the new token is read from k_new / v_new instead;
+//   - the softmax is online (running max / sum / rescaled accumulator, primer
+//     section 2.4); a unit with one chunk writes its output directly, otherwise
+//     each chunk writes (max, sum, accumulator) and a second small kernel merges
+//     the chunks with the same rescaling identity.  (A last-arriving-workgroup
+//     merge inside one kernel would need device-scope fences, which write back
+//     and invalidate the XCD's L2 on every workgroup.)
 #include "kev_internal.h"
+#include "kev_mfma_core.h"
 #include "../../include/kev.h"
 
 namespace kev {
 
 namespace {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-template <int CTRL>
-__device__ inline float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                 CTRL, 0xF, 0xF, false));
-}
-
-// Sum over groups of LANES (8 or 16) consecutive lanes; every lane gets the group sum.
-template <int LANES>
-__device__ inline float group_sum(float x) {
-    x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
-    x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
-    x += dpp<0x141>(x);   // row_half_mirror: 8-lane groups
-    if (LANES == 16) x += dpp<0x140>(x);   // row_mirror: 16-lane rows
-    return x;
-}
-
-__device__ inline float dot8(uint4 a, uint4 b, float acc) {
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), acc, false);
-    return acc;
-}
-
-__device__ inline void unpack8(uint4 u, float f[8]) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-        f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
-    }
-}
-
 __device__ inline uint16_t to_bf16(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-template <int D, int GMAX>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(DecodeArgs p) {
-    constexpr int NW = kDecodeWaves;
-    constexpr int DG = D / 8;          // lanes per row (8 bf16 each)
-    constexpr int RPI = 64 / DG;       // rows per wavefront instruction
-    constexpr int SB = 32;             // positions per online-softmax sub-block
-    constexpr int NI = SB / RPI;       // instructions per sub-block
-    __shared__ float w_m[NW][GMAX], w_l[NW][GMAX];
-    __shared__ float w_acc[NW][GMAX][D];
+using namespace core;
 
-    const int G = (GMAX == 1 || GMAX == 2 || GMAX == 4) ? GMAX : p.group;
+constexpr int DKT = 32;   // positions per staged tile
+
+// Direct loads of one 32-position K and V tile of a slot plane into one stage.  Rows past
+// the chunk end are clamped to its last row; the row of the new token comes from
+// k_new / v_new.
+template <int D>
+struct DecodeLoader {
+    static constexpr int IPT = DKT / Geom<D>::RPI;   // 1 KB loads per tensor per tile
+    DmaLane<D> ln[IPT];
+    const uint16_t *kbase, *vbase, *knew, *vnew;
+    int newpos, last;
+
+    __device__ __forceinline__ void issue(int k0, lds_t *ks, lds_t *vs) const {
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+            const int key = min(k0 + ln[i].row, last);
+            const bool nw = key == newpos;
+            const int64_t off = (int64_t)key * D + ln[i].coff;
+            dma16(nw ? knew + ln[i].coff : kbase + off, ks + i * Geom<D>::RPI * Geom<D>::ROWB);
+            dma16(nw ? vnew + ln[i].coff : vbase + off, vs + i * Geom<D>::RPI * Geom<D>::ROWB);
+        }
+    }
+};
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs p) {
+    constexpr int DC = D / 16, DB = D / 32;
+    constexpr int TB = DKT * D * 2;
+    constexpr int NI = 2 * DecodeLoader<D>::IPT;      // direct loads per tile
+    __shared__ __attribute__((aligned(1024))) char sk0[TB], sk1[TB], sk2[TB];
+    __shared__ __attribute__((aligned(1024))) char sv0[TB], sv1[TB], sv2[TB];
+    lds_t *K0 = (lds_t *)sk0, *K1 = (lds_t *)sk1, *K2 = (lds_t *)sk2;
+    lds_t *V0 = (lds_t *)sv0, *V1 = (lds_t *)sv1, *V2 = (lds_t *)sv2;
+
+    const int G = p.group;
     const int unit = blockIdx.x / p.max_chunks;
     const int c = blockIdx.x % p.max_chunks;
     const int r = unit / p.kv_heads, g = unit % p.kv_heads;
     const int slot = p.slot_ids[r];
     const int L = p.cache_lens[r];
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x;
     if (slot < 0 || slot >= p.n_slots) {
-        if (c == 0 && tid == 0) atomicOr(p.err, (int32_t)KEV_DEVERR_SLOT);
+        if (c == 0 && lane == 0) atomicOr(p.err, (int32_t)KEV_DEVERR_SLOT);
         return;
     }
     if (L < 1 || L > p.capacity) {
-        if (c == 0 && tid == 0) atomicOr(p.err, (int32_t)KEV_DEVERR_CACHE_LEN);
+        if (c == 0 && lane == 0) atomicOr(p.err, (int32_t)KEV_DEVERR_CACHE_LEN);
         return;
     }
     const int nchunks = (L + p.chunk - 1) / p.chunk;
@@ -107,195 +99,196 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(DecodeAr
     const uint16_t *knew = static_cast<const uint16_t *>(p.k_new) + ((int64_t)r * p.kv_heads + g) * D;
     const uint16_t *vnew = static_cast<const uint16_t *>(p.v_new) + ((int64_t)r * p.kv_heads + g) * D;
 
-    // In-place append of the new token (by the chunk that holds position L-1).
-    if (c == (L - 1) / p.chunk) {
-        if (tid < DG)
-            *reinterpret_cast<uint4 *>(kbase + (int64_t)(L - 1) * D + tid * 8) =
-                *reinterpret_cast<const uint4 *>(knew + tid * 8);
-        else if (tid < 2 * DG)
-            *reinterpret_cast<uint4 *>(vbase + (int64_t)(L - 1) * D + (tid - DG) * 8) =
-                *reinterpret_cast<const uint4 *>(vnew + (tid - DG) * 8);
+    // In-place append of the new token (by the chunk that holds position L-1).  This chunk
+    // reads that row from k_new / v_new, and no other chunk reads it, so the store needs
+    // no ordering against the loads below.
+    if (c == (L - 1) / p.chunk && lane < 2 * (D / 8)) {
+        const int part = lane % (D / 8);
+        uint16_t *dst = (lane < D / 8 ? kbase : vbase) + (int64_t)(L - 1) * D + part * 8;
+        const uint16_t *src = (lane < D / 8 ? knew : vnew) + part * 8;
+        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
     }
 
-    const int wave = tid >> 6, lane = tid & 63;
-    const int rg = lane / DG, dg = lane % DG;
+    const int p0 = c * p.chunk;
+    const int p1 = min(p0 + p.chunk, L);
+    const int n_tiles = (p1 - p0 + DKT - 1) / DKT;
+    DecodeLoader<D> ld;
+#pragma unroll
+    for (int i = 0; i < DecodeLoader<D>::IPT; ++i) ld.ln[i].init(i * Geom<D>::RPI);
+    ld.kbase = kbase;
+    ld.vbase = vbase;
+    ld.knew = knew;
+    ld.vnew = vnew;
+    ld.newpos = L - 1;
+    ld.last = p1 - 1;
 
-    uint4 qv[GMAX];
+    f32x16 o[DB];
 #pragma unroll
-    for (int h = 0; h < GMAX; ++h) {
-        qv[h] = make_uint4(0, 0, 0, 0);
-        if (h < G)
-            qv[h] = *reinterpret_cast<const uint4 *>(
-                static_cast<const uint16_t *>(p.q) + ((int64_t)r * p.heads + g * G + h) * D + dg * 8);
-    }
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const float cs = p.scale_log2;
 
-    float m[GMAX], l[GMAX], acc[GMAX][8];
-#pragma unroll
-    for (int h = 0; h < GMAX; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
-    }
+    ld.issue(p0, K0, V0);
+    if (n_tiles > 1) ld.issue(p0 + DKT, K1, V1);
 
-    const int per_wave = p.chunk / NW;
-    const int p0 = c * p.chunk + wave * per_wave;
-    const int p1 = min(p0 + per_wave, L);
-
-    for (int sb = p0; sb < p1; sb += SB) {
-        uint4 kr[NI], vr[NI];
+    // Query heads of this KV head are the MFMA columns: lane holds head (lane % 32).
+    const int col = lane & 31, half = lane >> 5;
+    bf16x8 qf[DC];
+    {
+        const uint16_t *qp = static_cast<const uint16_t *>(p.q) +
+                             ((int64_t)r * p.heads + g * G + col) * D + half * 8;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int pos = sb + i * RPI + rg;
-            kr[i] = make_uint4(0, 0, 0, 0);
-            vr[i] = make_uint4(0, 0, 0, 0);
-            if (pos < p1) {
-                const bool is_new = pos == L - 1;
-                kr[i] = *reinterpret_cast<const uint4 *>(is_new ? knew + dg * 8 : kbase + (int64_t)pos * D + dg * 8);
-                vr[i] = *reinterpret_cast<const uint4 *>(is_new ? vnew + dg * 8 : vbase + (int64_t)pos * D + dg * 8);
-            }
-        }
-        float s[NI][GMAX];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const bool live = sb + i * RPI + rg < p1;
-#pragma unroll
-            for (int h = 0; h < GMAX; ++h) {
-                if (h >= G) continue;
-                float x = group_sum<DG>(dot8(kr[i], qv[h], 0.f)) * p.scale_log2;
-                s[i][h] = live ? x : -INFINITY;
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < GMAX; ++h) {
-            if (h >= G) continue;
-            float mb = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < NI; ++i) mb = fmaxf(mb, s[i][h]);
-#pragma unroll
-            for (int o = DG; o < 64; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o));
-            const float m_new = fmaxf(m[h], mb);
-            const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);
-            m[h] = m_new;
-            float rs = 0.f;
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                s[i][h] = __builtin_amdgcn_exp2f(s[i][h] - m_new);
-                rs += s[i][h];
-            }
-            l[h] = l[h] * alpha + rs;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[h][j] *= alpha;
-        }
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            float vf[8];
-            unpack8(vr[i], vf);
-#pragma unroll
-            for (int h = 0; h < GMAX; ++h) {
-                if (h >= G) continue;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(s[i][h], vf[j], acc[h][j]);
-            }
+        for (int dc = 0; dc < DC; ++dc) {
+            uint4 u = make_uint4(0, 0, 0, 0);
+            if (col < G) u = *reinterpret_cast<const uint4 *>(qp + dc * 16);
+            qf[dc] = __builtin_bit_cast(bf16x8, u);
         }
     }
+    wait_vmcnt<0>();   // q, and the first two tiles issued before it, have landed
 
-    // Merge the row groups of the wavefront (they share m), then the wavefronts in LDS.
+    auto compute = [&](const lds_t *ks, const lds_t *vs, int k0) {
+        f32x16 s = scores1<D>(ks, 0, qf);
+        if (k0 + DKT > p1) {
 #pragma unroll
-    for (int h = 0; h < GMAX; ++h) {
-        if (h >= G) continue;
-#pragma unroll
-        for (int o = DG; o < 64; o <<= 1) {
-            l[h] += __shfl_xor(l[h], o);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[h][j] += __shfl_xor(acc[h][j], o);
-        }
-        if (lane < DG) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) w_acc[wave][h][dg * 8 + j] = acc[h][j];
-        }
-        if (lane == 0) {
-            w_m[wave][h] = m[h];
-            w_l[wave][h] = l[h];
-        }
-    }
-    __syncthreads();
-
-    float *part = p.partials + ((int64_t)unit * p.max_chunks) * G * (D + 2);
-    uint16_t *out = static_cast<uint16_t *>(p.out) + ((int64_t)r * p.heads + g * G) * D;
-    for (int e = tid; e < G * D; e += NW * 64) {
-        const int h = e / D, d = e % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, w_m[w][h]);
-        float A = 0.f, S = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float f = __builtin_amdgcn_exp2f(w_m[w][h] - M);
-            A = fmaf(f, w_acc[w][h][d], A);
-            S = fmaf(f, w_l[w][h], S);
-        }
-        if (nchunks == 1) {
-            out[h * D + d] = to_bf16(A / S);
-        } else {
-            float *pp = part + ((int64_t)c * G + h) * (D + 2);
-            pp[d] = A;
-            if (d == 0) {
-                pp[D] = M;
-                pp[D + 1] = S;
+            for (int i = 0; i < 16; ++i) {
+                const int key = k0 + (i >> 2) * 8 + half * 4 + (i & 3);
+                if (key >= p1) s[i] = -INFINITY;
             }
+        }
+        float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+        for (int i = 2; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
+        mx = max_halves(mx) * cs;
+        if (__any(mx > m_run + kLazy)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        }
+        const float mneg = -m_run;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+            f32x8 e;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                e[i] = __builtin_amdgcn_exp2f(fmaf(s[h8 * 8 + i], cs, mneg));
+                l_run += e[i];
+            }
+            pb[h8] = __builtin_convertvector(e, bf16x8);
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_frag<D>(vs, cc, db), pb[cc], o[db], 0, 0, 0);
+    };
+
+#define KEV_DSTEP(T, KC, VC, KN, VN)                                   \
+    {                                                                  \
+        if ((T) + 1 < n_tiles) wait_vmcnt<NI>();                       \
+        else wait_vmcnt<0>();                                          \
+        asm volatile("" ::: "memory");                                 \
+        if ((T) + 2 < n_tiles) ld.issue(p0 + ((T) + 2) * DKT, KN, VN); \
+        compute(KC, VC, p0 + (T) * DKT);                               \
+    }
+    for (int t = 0; t < n_tiles; t += 3) {
+        KEV_DSTEP(t, K0, V0, K2, V2)
+        if (t + 1 >= n_tiles) break;
+        KEV_DSTEP(t + 1, K1, V1, K0, V0)
+        if (t + 2 >= n_tiles) break;
+        KEV_DSTEP(t + 2, K2, V2, K1, V1)
+    }
+#undef KEV_DSTEP
+    wait_vmcnt<0>();
+
+    // Lanes l and l+32 hold the same head; rows d = db*32 + 8*(i/4) + 4*half + i%4.
+    const float l_tot = sum_halves(l_run);
+    if (col >= G) return;
+    if (nchunks == 1) {
+        const float inv = 1.f / l_tot;
+        uint16_t *op = static_cast<uint16_t *>(p.out) + ((int64_t)r * p.heads + g * G + col) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) f[j] = o[db][g4 * 4 + j] * inv;
+                *reinterpret_cast<bf16x4 *>(op + db * 32 + g4 * 8 + half * 4) = __builtin_convertvector(f, bf16x4);
+            }
+    } else {
+        float *pp = p.partials + (((int64_t)unit * p.max_chunks + c) * G + col) * (D + 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) f[j] = o[db][g4 * 4 + j];
+                *reinterpret_cast<f32x4 *>(pp + db * 32 + g4 * 8 + half * 4) = f;
+            }
+        if (half == 0) {
+            pp[D] = m_run;
+            pp[D + 1] = l_tot;
         }
     }
 }
 
-// Merge the chunk partials of every unit that spans more than one chunk.
+// Merge the chunk partials of every unit that spans more than one chunk.  One thread per
+// (head, d); all chunk loads are issued before any is used (one memory latency).
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs p) {
-    const int unit = blockIdx.x;
+    const int G = p.group;
+    const int e = blockIdx.x * 256 + threadIdx.x;          // over units x G x D
+    const int unit = e / (G * D);
+    if (unit >= p.n_req * p.kv_heads) return;
+    const int h = (e / D) % G, d = e % D;
     const int r = unit / p.kv_heads, g = unit % p.kv_heads;
     const int slot = p.slot_ids[r];
     const int L = p.cache_lens[r];
     if (slot < 0 || slot >= p.n_slots || L < 1 || L > p.capacity) return;
     const int nchunks = (L + p.chunk - 1) / p.chunk;
     if (nchunks == 1) return;
-    const int G = p.group;
-    const float *part = p.partials + ((int64_t)unit * p.max_chunks) * G * (D + 2);
-    uint16_t *out = static_cast<uint16_t *>(p.out) + ((int64_t)r * p.heads + g * G) * D;
-    for (int e = threadIdx.x; e < G * D; e += 256) {
-        const int h = e / D, d = e % D;
-        float M = -INFINITY;
-        for (int cc = 0; cc < nchunks; ++cc) M = fmaxf(M, part[((int64_t)cc * G + h) * (D + 2) + D]);
-        float A = 0.f, S = 0.f;
-        for (int cc = 0; cc < nchunks; ++cc) {
-            const float *pp = part + ((int64_t)cc * G + h) * (D + 2);
-            const float f = __builtin_amdgcn_exp2f(pp[D] - M);
-            A = fmaf(f, pp[d], A);
-            S = fmaf(f, pp[D + 1], S);
-        }
-        out[h * D + d] = to_bf16(A / S);
+    const float *part = p.partials + ((int64_t)unit * p.max_chunks * G + h) * (D + 2);
+    const int64_t cstride = (int64_t)G * (D + 2);
+    float mv[kDecodeMaxChunks], av[kDecodeMaxChunks], lv[kDecodeMaxChunks];
+#pragma unroll
+    for (int cc = 0; cc < kDecodeMaxChunks; ++cc) {
+        const bool ok = cc < nchunks;
+        const float *pp = part + cc * cstride;
+        mv[cc] = ok ? pp[D] : -INFINITY;
+        av[cc] = ok ? pp[d] : 0.f;
+        lv[cc] = ok ? pp[D + 1] : 0.f;
     }
-}
-
-template <int D, int GMAX>
-hipError_t launch(const DecodeArgs &a, hipStream_t s) {
-    const int64_t units = (int64_t)a.n_req * a.kv_heads;
-    hipLaunchKernelGGL((decode_bf16_kernel<D, GMAX>), dim3((unsigned)(units * a.max_chunks)),
-                       dim3(kDecodeWaves * 64), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.max_chunks == 1) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)units), dim3(256), 0, s, a);
-    return hipGetLastError();
+    float M = -INFINITY;
+#pragma unroll
+    for (int cc = 0; cc < kDecodeMaxChunks; ++cc) M = fmaxf(M, mv[cc]);
+    float A = 0.f, S = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < kDecodeMaxChunks; ++cc) {
+        const float f = __builtin_amdgcn_exp2f(mv[cc] - M);
+        A = fmaf(f, av[cc], A);
+        S = fmaf(f, lv[cc], S);
+    }
+    static_cast<uint16_t *>(p.out)[((int64_t)r * p.heads + g * G + h) * D + d] = to_bf16(A / S);
 }
 
 template <int D>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
-    switch (a.group) {
-    case 1: return launch<D, 1>(a, s);
-    case 2: return launch<D, 2>(a, s);
-    case 4: return launch<D, 4>(a, s);
-    case 8: return launch<D, 8>(a, s);
-    default: return launch<D, 8>(a, s);   // other group sizes up to 8, guarded by p.group
-    }
+    const int64_t units = (int64_t)a.n_req * a.kv_heads;
+    hipLaunchKernelGGL((decode_bf16_kernel<D>), dim3((unsigned)(units * a.max_chunks)), dim3(64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.max_chunks == 1) return e;
+    const int64_t threads = units * a.group * D;
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace

@@ -113,7 +113,8 @@ hipError_t launch_prefill_f32(const PrefillArgs &a, int32_t head_dim, int64_t gr
 hipError_t launch_decode_bf16(const DecodeArgs &a, int32_t head_dim, hipStream_t s);
 
 // Decode workgroup geometry.
-constexpr int32_t kDecodeWaves = 4;
-constexpr int32_t kDecodeChunk = 256;   // positions per workgroup (64 per wavefront)
+constexpr int32_t kDecodeWaves = 1;   // one wavefront per (request, KV head, chunk)
+constexpr int32_t kDecodeChunk = 256;      // positions per workgroup (doubled while a slot
+constexpr int32_t kDecodeMaxChunks = 16;   // would need more than kDecodeMaxChunks chunks)
 
 }  // namespace kev

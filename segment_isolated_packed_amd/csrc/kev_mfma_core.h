@@ -94,6 +94,24 @@ struct DmaLane {
     }
 };
 
+// S^T for the 32 keys [kb*32, kb*32+32) of a staged K tile.
+template <int D>
+__device__ __forceinline__ f32x16 scores1(const lds_t *ktile, int kb, const bf16x8 *qf) {
+    using G = Geom<D>;
+    const int lane = threadIdx.x & 63;
+    const int row = kb * 32 + (lane & 31), half = lane >> 5;
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+        const u32x4 a = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
+            ktile + G::off(row, 2 * dc + half));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[dc], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
 // S^T for both 32-key halves of a staged K tile (two independent MFMA chains, interleaved).
 template <int D>
 __device__ __forceinline__ void scores2(const lds_t *ktile, const bf16x8 *qf, f32x16 &s0, f32x16 &s1) {
@@ -156,19 +174,6 @@ __device__ __forceinline__ bf16x8 vt_frag(const lds_t *vtile, int c, int db) {
 // is read from the wrong register.
 __device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32); }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Sum of the 8 bf16 values of a P^T fragment (v_dot2_f32_bf16 against ones): the row sum
-// then counts exactly the rounded weights the PV MFMA uses.
-__device__ __forceinline__ float sum8(bf16x8 p, float acc) {
-    const u32x4 w = __builtin_bit_cast(u32x4, p);
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]), one, acc, false);
-    return acc;
-}
 
 // Online-softmax state of one lane (one query column; the lane pair l, l^32 shares it).
 // The running max is only moved (and O^T, l rescaled) when a new score exceeds it by more

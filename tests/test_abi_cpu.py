@@ -66,7 +66,7 @@ def test_decode_argument_checks(lib):
     assert _decode(lib, cap=0) == K.KEV_ERR_INVALID_ARG
     assert _decode(lib, dtype=1) == K.KEV_ERR_UNSUPPORTED
     assert _decode(lib, d=96) == K.KEV_ERR_UNSUPPORTED
-    assert _decode(lib, heads=72, kvh=4) == K.KEV_ERR_UNSUPPORTED      # group of 18
+    assert _decode(lib, heads=160, kvh=4) == K.KEV_ERR_UNSUPPORTED     # group of 40
     assert _decode(lib, n_req=9) == K.KEV_ERR_BAD_SLOT                  # more requests than slots
     assert _decode(lib, null=True) == K.KEV_ERR_INVALID_ARG
     assert _decode(lib, n_req=0) == K.KEV_OK

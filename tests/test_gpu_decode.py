@@ -41,7 +41,7 @@ def test_slot_decode_config(orc, full_case):
     assert np.array_equal(to_host_bits(pool), ref_pool)
 
 
-@pytest.mark.parametrize("hq,hk,d", [(32, 8, 128), (8, 8, 128), (16, 8, 128), (64, 8, 128),
+@pytest.mark.parametrize("hq,hk,d", [(32, 8, 128), (8, 8, 128), (16, 8, 128), (64, 8, 128), (256, 8, 128),
                                      (28, 4, 128), (8, 2, 64), (4, 1, 64)])
 def test_head_layouts_and_edges(orc, hq, hk, d):
     lens = [1, 2, 255, 256, 257, 511, 512, 513, 1000, 1023, 1024, 1025]
