@@ -149,9 +149,10 @@ int kev_get_device_errors(void *stream, int32_t *flags_out);
  *
  * kev_schedule_host: the work list computed on the host from a HOST copy of
  * cu_seqlens: items_out[2*i] = question, items_out[2*i+1] = query block, in
- * the order the device scheduler uses (query block descending, so the
- * longest items start first).  Returns KEV_OK and *n_items_out, or
- * KEV_ERR_INVALID_ARG if max_items is too small.
+ * the order the device scheduler uses: question by question, questions in
+ * descending number of query blocks (ties by index here, in an unspecified
+ * order on the device), query block descending inside a question.  Returns
+ * KEV_OK and *n_items_out, or KEV_ERR_INVALID_ARG if max_items is too small.
  *
  * kev_schedule_device: runs the device scheduler kernel on device cu_seqlens
  * and copies its work list to the host buffer items_out (synchronises).

@@ -202,13 +202,12 @@ int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
     pa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
     if (dtype == KEV_BF16) {
         const PrefillShape sh = prefill_shape_bf16(heads, kv_heads);
-        pa.heads_per_wg = sh.heads_per_wg;
         pa.row_blocks = sh.row_blocks;
         pa.block_rows = sh.block_rows;
-        pa.n_hgroups = heads / sh.heads_per_wg;
-        const int64_t grid = n_max * pa.n_hgroups;
+        pa.wg_per_kvh = sh.wg_per_kvh;
+        const int64_t grid = n_max * kv_heads * sh.wg_per_kvh;
         if (grid > INT32_MAX) return KEV_ERR_INVALID_ARG;
-        return to_status(launch_prefill_bf16(pa, head_dim, sh.waves, grid, stream));
+        return to_status(launch_prefill_bf16(pa, head_dim, grid, stream));
     }
     pa.heads_per_wg = 1;
     pa.row_blocks = 1;
@@ -312,19 +311,17 @@ int kev_schedule_host(const int32_t *cu, int32_t n_seg, int32_t block_rows, int3
     int rc = host_check_seqlens(cu, n_seg, cu[n_seg]);
     if (rc) return rc;
     std::vector<int32_t> nb(n_seg), order(n_seg);
-    int32_t maxnb = 0;
     int64_t total = 0;
     for (int32_t s = 0; s < n_seg; ++s) {
         nb[s] = qblocks(cu[s + 1] - cu[s], block_rows);
-        maxnb = std::max(maxnb, nb[s]);
         total += nb[s];
         order[s] = s;
     }
     if (total > max_items_ || (total > 0 && !items_out)) return KEV_ERR_INVALID_ARG;
     std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return nb[x] > nb[y]; });
     int64_t p = 0;
-    for (int32_t t = maxnb - 1; t >= 0; --t)
-        for (int32_t i = 0; i < n_seg && nb[order[i]] > t; ++i) {
+    for (int32_t i = 0; i < n_seg; ++i)
+        for (int32_t t = nb[order[i]] - 1; t >= 0; --t) {
             items_out[2 * p] = order[i];
             items_out[2 * p + 1] = t;
             ++p;

@@ -13,9 +13,9 @@ namespace kev {
 // t covers rows [t*block_rows, min((t+1)*block_rows, L)) of the question and
 // needs keys [0, min((t+1)*block_rows, L)) of the same question: everything at
 // or left of its diagonal and nothing of any other question.  Work items are
-// (question, query block) pairs; all items of one query-block index t cost the
-// same (t+1 blocks of keys), so listing them with t descending starts the
-// longest items first.
+// (question, query block) pairs; item t costs t+1 blocks of keys.  They are
+// listed question by question (longest question first), t descending inside a
+// question.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int32_t qblocks(int32_t len, int32_t block_rows) {
     return len <= 0 ? 0 : (len + block_rows - 1) / block_rows;
@@ -27,23 +27,22 @@ __host__ __device__ inline int64_t max_items(int64_t total_tokens, int64_t n_seg
     return (total_tokens + block_rows - 1) / block_rows + n_seg;
 }
 
-// Rows per query block and heads per workgroup chosen for a head layout.
+// bf16 path: an item of 32*R rows holds G*R (head, 32-row block) units per KV head, one
+// wavefront each, in workgroups of 4 wavefronts; R is the smallest power of two that makes
+// G*R a multiple of 4.
 struct PrefillShape {
-    int32_t heads_per_wg;   // query heads of one KV group handled together (shares K/V tiles)
-    int32_t row_blocks;     // 32-row blocks per item (one wavefront each, per head)
-    int32_t block_rows;     // 32 * row_blocks
-    int32_t waves;          // heads_per_wg * row_blocks
+    int32_t row_blocks;     // R
+    int32_t block_rows;     // 32 * R
+    int32_t wg_per_kvh;     // G * R / 4 workgroups per item and KV head
 };
 
+constexpr int32_t kPrefillUnitsPerWg = 4;   // wavefronts per workgroup
+
 inline PrefillShape prefill_shape_bf16(int32_t heads, int32_t kv_heads) {
-    int32_t G = heads / kv_heads;
-    int32_t gw = 1;
-    for (int32_t c = 8; c >= 1; --c)
-        if (G % c == 0) { gw = c; break; }
-    int32_t r = 8 / gw;
-    if (r > 4) r = 4;
-    if (r < 1) r = 1;
-    return PrefillShape{gw, r, 32 * r, gw * r};
+    const int32_t G = heads / kv_heads;
+    int32_t r = 1;
+    while ((G * r) % kPrefillUnitsPerWg != 0) r *= 2;
+    return PrefillShape{r, 32 * r, G * r / kPrefillUnitsPerWg};
 }
 
 constexpr int32_t kF32BlockRows = 64;   // fp32 path: one wavefront of 64 rows per item and head
@@ -63,18 +62,18 @@ struct ScheduleArgs {
 
 // Workspace layout of the scheduler (int32 units):
 //   [0] n_items  [1] flags  [2..] hist[hist_len] | fill[hist_len] | cnt[hist_len] |
-//   start[hist_len] | sigma[n_seg] | items[2 * max_items]
+//   sigma[n_seg] | qoff[n_seg] | items[2 * max_items]
 struct ScheduleLayout {
-    int64_t hist, fill, cnt, start, sigma, items, total;
+    int64_t hist, fill, cnt, sigma, qoff, items, total;
 };
 __host__ __device__ inline ScheduleLayout schedule_layout(int32_t n_seg, int32_t hist_len, int64_t n_max_items) {
     ScheduleLayout L;
     L.hist = 4;
     L.fill = L.hist + hist_len;
     L.cnt = L.fill + hist_len;
-    L.start = L.cnt + hist_len;
-    L.sigma = L.start + hist_len;
-    L.items = (L.sigma + n_seg + 3) & ~int64_t(3);
+    L.sigma = L.cnt + hist_len;
+    L.qoff = L.sigma + n_seg;
+    L.items = (L.qoff + n_seg + 3) & ~int64_t(3);
     L.total = L.items + 2 * n_max_items;
     return L;
 }
@@ -86,7 +85,8 @@ struct PrefillArgs {
     const int32_t *sched;     // scheduler workspace (n_items at [0], items at items_off)
     int64_t items_off;
     int32_t heads, kv_heads, group;     // group = heads / kv_heads
-    int32_t heads_per_wg, row_blocks, block_rows, n_hgroups;
+    int32_t heads_per_wg, row_blocks, block_rows, n_hgroups;   // fp32 path
+    int32_t wg_per_kvh;                 // bf16 path: workgroups per item and KV head
     float scale_log2;                   // log2(e) / sqrt(head_dim)
 };
 
@@ -106,8 +106,8 @@ struct DecodeArgs {
 
 // Launchers (each lives in the translation unit of its kernel).
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
-hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int32_t waves,
-                               int64_t grid, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int64_t grid,
+                               hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, int32_t head_dim, int64_t grid,
                               hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, int32_t head_dim, hipStream_t s);

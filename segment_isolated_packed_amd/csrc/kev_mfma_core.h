@@ -80,6 +80,20 @@ __device__ __forceinline__ void dma16(const void *g, const lds_t *lds_base) {
                  : "memory");
 }
 
+// Same load with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset
+// (the global address is base + voff), so the per-tile address step is one scalar add.
+__device__ __forceinline__ void dma16s(const void *base, unsigned voff, unsigned lds_addr) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+    const uint64_t sb = ((uint64_t)hi << 32) | lo;
+    const unsigned m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sb), "s"(m0v)
+                 : "memory");
+}
+
 // Per-lane part of a direct load of tile rows [r0, r0 + RPI): the row this lane fills and
 // the global chunk that belongs at its LDS position (chunk c ^ swz(r) of the row).
 template <int D>
@@ -112,43 +126,15 @@ __device__ __forceinline__ f32x16 scores1(const lds_t *ktile, int kb, const bf16
     return acc;
 }
 
-// S^T for both 32-key halves of a staged K tile (two independent MFMA chains, interleaved).
+// K fragment (A operand of S^T) for k step dc of a staged 32-key K tile: lane l holds
+// row l%32, d = dc*16 + (l/32)*8 .. +8.
 template <int D>
-__device__ __forceinline__ void scores2(const lds_t *ktile, const bf16x8 *qf, f32x16 &s0, f32x16 &s1) {
+__device__ __forceinline__ bf16x8 k_frag(const lds_t *ktile, int dc) {
     using G = Geom<D>;
     const int lane = threadIdx.x & 63;
     const int row = lane & 31, half = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        s0[i] = 0.f;
-        s1[i] = 0.f;
-    }
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-        const int off = G::off(row, 2 * dc + half);
-        const u32x4 a0 = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(ktile + off);
-        const u32x4 a1 = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(ktile + off + 32 * G::ROWB);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), qf[dc], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), qf[dc], s1, 0, 0, 0);
-    }
-}
-
-// S^T for the 32 keys [kb*32, kb*32+32) of a staged K tile against the wave's query columns.
-template <int D>
-__device__ __forceinline__ f32x16 scores(const lds_t *ktile, int kb, const bf16x8 *qf) {
-    using G = Geom<D>;
-    const int lane = threadIdx.x & 63;
-    const int row = kb * 32 + (lane & 31), half = lane >> 5;
-    f32x16 acc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-        const u32x4 u = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
-            ktile + G::off(row, 2 * dc + half));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), qf[dc], acc, 0, 0, 0);
-    }
-    return acc;
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
+                                          ktile + G::off(row, 2 * dc + half)));
 }
 
 // V^T fragment (A operand) for d-block db and 16-key chunk c of a staged V tile.
@@ -169,11 +155,18 @@ __device__ __forceinline__ bf16x8 vt_frag(const lds_t *vtile, int c, int db) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// Max / sum over lanes l and l^32 (every lane gets the value for its pair).  ds_bpermute;
-// the gfx950 v_permlane32_swap builtin is not used: in this compiler its second result
-// is read from the wrong register.
+// Max / sum over lanes l and l^32 (every lane gets the value for its pair).  ds_bpermute
+// through the LDS unit: its wait also waits for every LDS read issued before it.
 __device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32); }
+
+// Max over lanes l and l^32 on the VALU (v_permlane32_swap: with both operands holding x,
+// one result holds the low half twice and the other the high half twice), so no LDS
+// instruction and no wait on earlier LDS reads is involved.
+__device__ __forceinline__ float max_halves_valu(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // Online-softmax state of one lane (one query column; the lane pair l, l^32 shares it).
 // The running max is only moved (and O^T, l rescaled) when a new score exceeds it by more

@@ -10,15 +10,24 @@
 // softmax kept as a running max, running sum and rescaled accumulator that are
 // corrected whenever a later block raises the max (primer, section 2.4).
 //
-// Work item = (question, block of 32*R query rows) from the scheduler, times a
-// group of `heads_per_wg` query heads that share one KV head.  One wavefront
-// owns 32 query rows of one head.  All wavefronts of a workgroup read the same
-// K/V tiles (64 keys) from LDS, so each tile load serves heads_per_wg * R
-// wavefronts.  Only key tiles inside the item's own question and at or left of
-// its diagonal are loaded; inside a tile, 32-key sub-blocks that lie entirely
-// above a wavefront's rows are skipped and the causal select (-inf, not a
-// multiply) is applied only to sub-blocks that cross the diagonal or the end
-// of the question.
+// Decomposition.  A work item from the scheduler is (question, block of 32*R
+// query rows); per KV head it holds G*R units of (query head of the group,
+// 32-row block), one wavefront each.  R is the smallest power of two with G*R
+// a multiple of 4, so the units fill workgroups of exactly 4 wavefronts (one
+// per SIMD).  Unit u of workgroup w is u = 4w + wave, with row block u / G and
+// head u % G: a workgroup spans at most two adjacent row blocks, so its waves
+// need nearly the same keys.  All four read the same K/V tiles from LDS.
+//
+// Placement.  Workgroups are dealt to the 8 XCDs round-robin by index, and
+// each XCD has its own L2.  The KV head is the fastest-varying part of the
+// workgroup index, so when kv_heads divides 8 every XCD serves a single KV
+// head; with the scheduler's question-major order, the workgroups resident on
+// one XCD then read the K/V rows of one (question, KV head) from its L2.
+//
+// Occupancy.  A workgroup uses 64 KB of LDS and at most 256 registers per lane,
+// so two workgroups share each CU and every SIMD runs two wavefronts that belong
+// to different workgroups.  Their barriers are independent, so one wavefront's
+// MFMA work can overlap the other's softmax work.
 //
 // MFMA orientation (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
 //   S^T[key][q] = K_tile[key][:] . Q^T[:][q]     A = K from LDS, B = Q in VGPRs
@@ -29,12 +38,20 @@
 // the first one's accumulators (converted to bf16).  Staging and operand reads
 // are described in kev_mfma_core.h.
 //
-// Pipeline: three LDS stages per tensor.  At tile t every wavefront waits for
-// its own direct loads of tile t, meets the others at one barrier (which also
-// retires all reads of tile t-1), issues the loads of tile t+2 into the stage
-// tile t-1 used, and computes tile t.  The stages are separate __shared__
-// arrays so the compiler can see that reads of one stage never alias loads
-// in flight to another.
+// Pipeline.  Tiles are 32 keys.  K and V each have four LDS stages and direct
+// loads run three tiles ahead.  Iteration j starts with the scores of tile j
+// already issued on MFMA.  The wavefront waits for its own loads of K(j+1) and
+// V(j), meets the others at one barrier (which also retires all reads of K(j)
+// and V(j-1), so their stages take K(j+4) and V(j+3)), reads every fragment of
+// K(j+1) and V(j) into registers at once, takes the softmax of tile j while
+// those reads land, runs P.V of tile j and issues the scores of tile j+1, which
+// execute while it waits at the next barrier.  The loop is unrolled by the
+// stage count, so all LDS addresses carry the stage as an immediate offset.
+// Only tiles inside the item's own question and at or left of its diagonal are
+// loaded; the causal select (-inf, not a multiply) is applied only to tiles
+// that cross a wavefront's diagonal or the end of the question.
+#include <type_traits>
+
 #include "kev_internal.h"
 #include "kev_mfma_core.h"
 
@@ -44,145 +61,203 @@ namespace {
 
 using namespace core;
 
-constexpr int KT = 64;   // keys per tile
+constexpr int KT = 32;      // keys per tile
+constexpr int NWAVE = 4;    // wavefronts per workgroup
+constexpr int NS = 4;       // LDS stages per tensor (loads run NS-1 tiles ahead)
 
-template <int D, int NW>
+template <int D>
 struct Cfg {
     static constexpr int DC = D / 16;                    // k steps of the S MFMA
     static constexpr int DB = D / 32;                    // 32-row d blocks of O^T
-    static constexpr int IPT = KT / Geom<D>::RPI;        // direct loads per K (or V) tile
-    static constexpr int NIT = (IPT + NW - 1) / NW;      // per wavefront per tensor (uniform)
-    static constexpr int NI = 2 * NIT;                   // per wavefront per tile
+    static constexpr int RPI = Geom<D>::RPI;             // tile rows per direct load
+    static constexpr int IPT = KT / RPI;                 // direct loads per K (or V) tile
+    static constexpr int NIT = IPT / NWAVE;              // per wavefront per tensor (4 waves)
     static constexpr int TB = KT * D * 2;                // bytes per tile
+    static constexpr int LDS = 2 * NS * TB;
+    static_assert(IPT % NWAVE == 0 && NIT >= 1, "loads must split evenly");
 };
 
-// Direct loads of one K and V tile into one stage.  Every wavefront issues exactly NIT
-// loads per tensor (a few re-issue another wavefront's load when NW does not divide the
-// count; same data, same place), so one vmcnt value fits all.  Rows past key_end are
-// clamped to key_end-1: a valid row of the same question, so nothing outside the question
-// is read and staged values stay finite wherever the question's own values are.
+// Direct loads of K or V tiles by NW wavefronts.  Wavefront w fills tile rows
+// ((w + NW*i) mod IPT) * RPI .. +RPI for i < NIT; when NW exceeds the number of loads per
+// tile, several wavefronts issue the same load (same data to the same place), so every
+// wavefront issues exactly NIT loads per tile and one vmcnt value fits all.  The global
+// address is a wave-uniform tile base plus a per-lane offset that is the same for every
+// full tile.  In the tile that holds key_end, rows at or past key_end are clamped to
+// key_end - 1: a row of the same question, so nothing outside it is read.
 template <int D, int NW>
 struct TileLoader {
-    using C = Cfg<D, NW>;
-    DmaLane<D> ln[C::NIT];
-    int r0[C::NIT];
-    int64_t stride;
-    const uint16_t *kg, *vg;
+    static constexpr int RPI = Geom<D>::RPI;
+    static constexpr int IPT = KT / RPI;
+    static constexpr int NIT = (IPT + NW - 1) / NW;
+    unsigned voff[NIT];     // byte offset of this lane's chunk inside a full tile
+    unsigned lds_row[NIT];  // LDS byte offset of the load's first row inside a stage
+    const char *kbase, *vbase;  // tile 0
+    int64_t tile_step;          // bytes between consecutive tiles
+    int row_bytes;
+    int key_end;
 
-    __device__ void init(const uint16_t *k, const uint16_t *v, int64_t row_stride) {
-        const int wave = threadIdx.x >> 6;
-        kg = k;
-        vg = v;
-        stride = row_stride;
+    __device__ static int first_row(int wave, int i) { return ((wave + NW * i) % IPT) * RPI; }
+
+    __device__ void init(const uint16_t *k, const uint16_t *v, int64_t row_stride, int kend, int wave) {
+        kbase = reinterpret_cast<const char *>(k);
+        vbase = reinterpret_cast<const char *>(v);
+        row_bytes = (int)(row_stride * 2);
+        tile_step = (int64_t)row_bytes * KT;
+        key_end = kend;
 #pragma unroll
-        for (int i = 0; i < C::NIT; ++i) {
-            r0[i] = ((wave + NW * i) % C::IPT) * Geom<D>::RPI;
-            ln[i].init(r0[i]);
+        for (int i = 0; i < NIT; ++i) {
+            DmaLane<D> ln;
+            const int r0 = first_row(wave, i);
+            ln.init(r0);
+            voff[i] = (unsigned)(ln.row * row_bytes + ln.coff * 2);
+            lds_row[i] = (unsigned)(r0 * Geom<D>::ROWB);
         }
     }
 
-    __device__ __forceinline__ void issue(int tile, int key_end, lds_t *ks, lds_t *vs) const {
+    __device__ __forceinline__ void issue(const char *base, int tile, unsigned stage_addr, int wave) const {
         const int k0 = tile * KT;
-        const bool full = k0 + KT <= key_end;
+        const char *tb = base + (int64_t)tile * tile_step;
+        if (k0 + KT <= key_end) {
 #pragma unroll
-        for (int i = 0; i < C::NIT; ++i) {
-            const int key = full ? k0 + ln[i].row : min(k0 + ln[i].row, key_end - 1);
-            const int64_t off = (int64_t)key * stride + ln[i].coff;
-            dma16(kg + off, ks + r0[i] * Geom<D>::ROWB);
-            dma16(vg + off, vs + r0[i] * Geom<D>::ROWB);
+            for (int i = 0; i < NIT; ++i) dma16s(tb, voff[i], stage_addr + lds_row[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NIT; ++i) {
+                DmaLane<D> ln;
+                ln.init(first_row(wave, i));
+                const int r = min(k0 + ln.row, key_end - 1) - k0;
+                dma16s(tb, (unsigned)(r * row_bytes + ln.coff * 2), stage_addr + lds_row[i]);
+            }
         }
     }
 };
 
-// One wavefront's work on a staged tile: 32 query rows (row0 ..) against keys k0 .. k0+63.
-// `edge` marks the tile that crosses this wavefront's diagonal or the question's end; only
-// there are scores masked (a select to -inf).
+// Online-softmax state of one lane (one query row; the lane pair l, l^32 shares it).
+// The running max is only moved (and O^T, l rescaled) when a new score exceeds it by more
+// than kLazy (log2 units); otherwise weights are taken against the stale max, so they stay
+// below 2^kLazy.  Either way out = O / l is the same softmax average.
 template <int D>
-__device__ __forceinline__ void compute_tile(const lds_t *ks, const lds_t *vs, int k0, bool edge,
-                                             int qrow, int L, float c, const bf16x8 *qf,
-                                             f32x16 *o, float &m_run, float &l_run) {
-    constexpr int DB = D / 32;
-    const int half = (threadIdx.x & 63) >> 5;
-    f32x16 s[2];
-    scores2<D>(ks, qf, s[0], s[1]);
-    if (edge) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = k0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-                if (key > qrow || key >= L) s[kb][i] = -INFINITY;
-            }
-    }
-    float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-    for (int i = 2; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[0][i]), s[0][i + 1]);
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[1][i]), s[1][i + 1]);
-    mx = max_halves(mx) * c;
+struct RowState {
+    f32x16 o[D / 32];
+    float m, l, alpha;
+    bool pending;   // O^T still has to be multiplied by alpha
+};
 
-    // lazy rescale: move the running max only when some row grew by more than kLazy
-    if (__any(mx > m_run + kLazy)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+// Row max of a scored (and, where needed, masked) 32-key tile and the lazy update of the
+// running max; l is rescaled here, O^T by apply_rescale before the next P.V product.
+template <int D>
+__device__ __forceinline__ void tile_max(const f32x16 &s, float c, RowState<D> &st) {
+    float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    for (int i = 2; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
+    mx = max_halves_valu(mx) * c;
+    st.pending = __any(mx > st.m + kLazy);
+    if (st.pending) {
+        const float m_new = fmaxf(st.m, mx);
+        st.alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+        st.m = m_new;
+        st.l *= st.alpha;
     }
-    const float mneg = -m_run;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int h8 = 0; h8 < 2; ++h8) {
-            f32x8 e;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                e[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][h8 * 8 + i], c, mneg));
-                l_run += e[i];
-            }
-            pb[kb * 2 + h8] = __builtin_convertvector(e, bf16x8);
-        }
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_frag<D>(vs, cc, db), pb[cc], o[db], 0, 0, 0);
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
-    using C = Cfg<D, NW>;
-    __shared__ __attribute__((aligned(1024))) char sk0[C::TB], sk1[C::TB], sk2[C::TB];
-    __shared__ __attribute__((aligned(1024))) char sv0[C::TB], sv1[C::TB], sv2[C::TB];
-    lds_t *K0 = (lds_t *)sk0, *K1 = (lds_t *)sk1, *K2 = (lds_t *)sk2;
-    lds_t *V0 = (lds_t *)sv0, *V1 = (lds_t *)sv1, *V2 = (lds_t *)sv2;
+// P = exp2(S*c - m) in bf16 (two 16-key chunks) with the row sums in fp32.
+template <int D>
+__device__ __forceinline__ void tile_p(const f32x16 &s, float c, RowState<D> &st, bf16x8 *pb) {
+    const float mneg = -st.m;
+    float part[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+        f32x8 e;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s[cc * 8 + i], c, mneg));
+        part[cc] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        pb[cc] = __builtin_convertvector(e, bf16x8);
+    }
+    st.l += part[0] + part[1];
+}
+
+// O^T += V^T P^T with the V^T fragments of the tile in registers (vf[cc * DB + db]:
+// 16-key chunk cc, d block db).
+template <int D>
+__device__ __forceinline__ void tile_o(const bf16x8 *pb, const bf16x8 *vf, RowState<D> &st) {
+    constexpr int DB = D / 32;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cc * DB + db], pb[cc], st.o[db], 0, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void tile_pv(const f32x16 &s, const bf16x8 *vf, float c, RowState<D> &st) {
+    bf16x8 pb[2];
+    tile_p<D>(s, c, st, pb);
+    tile_o<D>(pb, vf, st);
+}
+
+template <int D>
+__device__ __forceinline__ void apply_rescale(RowState<D> &st) {
+    if (st.pending) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st.o[db][i] *= st.alpha;
+        st.pending = false;
+    }
+}
+
+// Causal / question-end select on a 32-key tile that crosses the diagonal or the end.
+template <int D>
+__device__ __forceinline__ void mask_tile(f32x16 &s, int k0, int qrow, int L) {
+    const int half = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int key = k0 + (i >> 2) * 8 + half * 4 + (i & 3);
+        if (key > qrow || key >= L) s[i] = -INFINITY;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_bf16_kernel(PrefillArgs p) {
+    using C = Cfg<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    const unsigned lds0 = (unsigned)(uintptr_t)(lds_t *)smem;
+    // K stages at [0, NS*TB), V stages after them.
+    auto kst = [&](int s) { return (lds_t *)smem + s * C::TB; };
+    auto vst = [&](int s) { return (lds_t *)smem + (NS + s) * C::TB; };
 
     const int32_t n_items = p.sched[0];
-    const int item = blockIdx.x / p.n_hgroups;
+    const int per_item = p.kv_heads * p.wg_per_kvh;
+    const int item = blockIdx.x / per_item;
     if (item >= n_items) return;
-    const int hg = blockIdx.x % p.n_hgroups;
+    const int rem = blockIdx.x - item * per_item;
+    const int kvh = rem % p.kv_heads, w = rem / p.kv_heads;   // KV head fastest: see above
     const int32_t *it = p.sched + p.items_off + 2 * item;
     const int seg = it[0], t = it[1];
     const int a = p.cu[seg], L = p.cu[seg + 1] - a;
+    const int G = p.group;
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int item_row0 = t * p.block_rows;
+    const int wg_row_lo = item_row0 + ((NWAVE * w) / G) * 32;
+    if (wg_row_lo >= L) return;   // every wavefront of this workgroup is past the question
+    const int wg_key_end = min(item_row0 + ((NWAVE * w + NWAVE - 1) / G + 1) * 32, L);
+    const int n_tiles = (wg_key_end + KT - 1) / KT;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
-    const int hw = wave % p.heads_per_wg, rb = wave / p.heads_per_wg;
-    const int head = hg * p.heads_per_wg + hw;
-    const int kvh = (hg * p.heads_per_wg) / p.group;
+    const int u = NWAVE * w + wave;
+    const int rb = u / G;
+    const int head = kvh * G + (u - rb * G);
+    const int row0 = item_row0 + rb * 32;                       // question-relative
+    const int wave_key_end = row0 < L ? min(row0 + 32, L) : 0;
+    const int my_tiles = (wave_key_end + KT - 1) / KT;
+    const int n_full = min(row0 + 1, L) / KT;                   // tiles needing no mask
 
-    const int row0 = t * p.block_rows + rb * 32;                 // question-relative
-    const int item_key_end = min((t + 1) * p.block_rows, L);
-    const int wave_key_end = row0 < L ? min(row0 + 32, L) : 0;  // keys this wavefront needs
-    const int n_tiles = (item_key_end + KT - 1) / KT;
-
+    const int64_t kv_stride = (int64_t)p.kv_heads * D;
     const uint16_t *kg = static_cast<const uint16_t *>(p.k) + ((int64_t)a * p.kv_heads + kvh) * D;
     const uint16_t *vg = static_cast<const uint16_t *>(p.v) + ((int64_t)a * p.kv_heads + kvh) * D;
-    const int64_t kv_stride = (int64_t)p.kv_heads * D;
 
     // Q^T operand: lane holds q row (row0 + col), d = dc*16 + half*8 .. +8.
     const int qrow = row0 + col;
@@ -192,50 +267,105 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
                              ((int64_t)(a + qrow) * p.heads + head) * D + half * 8;
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc) {
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (qrow < L) u = *reinterpret_cast<const uint4 *>(qp + dc * 16);
-            qf[dc] = __builtin_bit_cast(bf16x8, u);
+            uint4 v4 = make_uint4(0, 0, 0, 0);
+            if (qrow < L) v4 = *reinterpret_cast<const uint4 *>(qp + dc * 16);
+            qf[dc] = __builtin_bit_cast(bf16x8, v4);
         }
     }
-
     wait_vmcnt<0>();   // q is in registers before any direct load is in flight
 
-    f32x16 o[C::DB];
+    RowState<D> st;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+        for (int i = 0; i < 16; ++i) st.o[db][i] = 0.f;
+    st.m = -INFINITY;
+    st.l = 0.f;
+    st.alpha = 1.f;
+    st.pending = false;
     const float c = p.scale_log2;
 
-    TileLoader<D, NW> ld;
-    ld.init(kg, vg, kv_stride);
-    ld.issue(0, item_key_end, K0, V0);
-    if (n_tiles > 1) ld.issue(1, item_key_end, K1, V1);
+    TileLoader<D, NWAVE> ld;
+    ld.init(kg, vg, kv_stride, wg_key_end, wave);
+    auto kaddr = [&](int s) { return lds0 + (unsigned)(s * C::TB); };
+    auto vaddr = [&](int s) { return lds0 + (unsigned)((NS + s) * C::TB); };
 
-#define KEV_STEP(T, KC, VC, KN, VN)                                                           \
-    {                                                                                          \
-        if ((T) + 1 < n_tiles) wait_vmcnt<C::NI>();                                            \
-        else wait_vmcnt<0>();                                                                  \
-        barrier();                                                                             \
-        if ((T) + 2 < n_tiles) ld.issue((T) + 2, item_key_end, KN, VN);                       \
-        if ((T) * KT < wave_key_end)                                                           \
-            compute_tile<D>(KC, VC, (T) * KT, (T) * KT + KT - 1 > row0 || (T) * KT + KT > L,     \
-                            qrow, L, c, qf, o, m_run, l_run);                                  \
+    // Issue order: K(0); then, per (virtual) iteration i, K(i+NS) and V(i+NS-1).  At the
+    // barrier of iteration j the wave needs K(j+1) and V(j), both issued at iteration
+    // j-NS+1 with V last; the loads of at most NS-2 later iterations may stay in flight.
+    ld.issue(ld.kbase, 0, kaddr(0), wave);
+    for (int i = 1 - NS; i < 0; ++i) {
+        if (i + NS < n_tiles) ld.issue(ld.kbase, i + NS, kaddr(i + NS), wave);
+        if (i + NS - 1 < n_tiles) ld.issue(ld.vbase, i + NS - 1, vaddr(i + NS - 1), wave);
     }
-    for (int kt = 0; kt < n_tiles; kt += 3) {
-        KEV_STEP(kt, K0, V0, K2, V2)
-        if (kt + 1 >= n_tiles) break;
-        KEV_STEP(kt + 1, K1, V1, K0, V0)
-        if (kt + 2 >= n_tiles) break;
-        KEV_STEP(kt + 2, K2, V2, K1, V1)
+    if (n_tiles >= NS) wait_vmcnt<2 * C::NIT * (NS - 1)>();   // K(0) has landed
+    else wait_vmcnt<0>();
+    barrier();
+
+    bf16x8 kf[C::DC];             // K fragments of the next tile to score
+    bf16x8 vf[2 * C::DB];         // V^T fragments of the current tile
+    f32x16 s;                     // scores of the current tile
+    auto score = [&]() {
+        f32x16 acc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int dc = 0; dc < C::DC; ++dc)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dc], qf[dc], acc, 0, 0, 0);
+        return acc;
+    };
+    if (my_tiles > 0) {
+#pragma unroll
+        for (int dc = 0; dc < C::DC; ++dc) kf[dc] = k_frag<D>(kst(0), dc);
+        s = score();
     }
-#undef KEV_STEP
+
+    // Iteration j: the scores of tile j are in flight on MFMA.  After the barrier the wave
+    // reads all fragments of K(j+1) and V(j) at once, takes the softmax of tile j while
+    // those reads land, runs P.V of tile j and issues the scores of tile j+1, which then
+    // execute while the wave waits at the next barrier.
+    // The loop is unrolled by NS so every stage address is a compile-time offset.
+    auto iteration = [&](const int j, auto U) {
+        constexpr int u = decltype(U)::value;   // j % NS
+        if (j + NS - 1 < n_tiles) wait_vmcnt<2 * C::NIT * (NS - 2)>();
+        else wait_vmcnt<0>();
+        barrier();
+        if (j + NS < n_tiles) ld.issue(ld.kbase, j + NS, kaddr(u), wave);
+        if (j + NS - 1 < n_tiles) ld.issue(ld.vbase, j + NS - 1, vaddr((u + NS - 1) % NS), wave);
+        if (j < my_tiles) {
+            const lds_t *kn = kst((u + 1) % NS);   // past the last tile: an unused read
+            const lds_t *vc = vst(u);
+#pragma unroll
+            for (int dc = 0; dc < C::DC; ++dc) kf[dc] = k_frag<D>(kn, dc);
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) vf[cc * C::DB + db] = vt_frag<D>(vc, cc, db);
+            if (j >= n_full) mask_tile<D>(s, j * KT, qrow, L);
+            tile_max<D>(s, c, st);
+            apply_rescale<D>(st);
+            tile_pv<D>(s, vf, c, st);
+            if (j + 1 < my_tiles) s = score();
+        }
+    };
+    for (int j0 = 0; j0 < n_tiles; j0 += NS) {
+        iteration(j0, std::integral_constant<int, 0>{});
+        if (j0 + 1 >= n_tiles) break;
+        iteration(j0 + 1, std::integral_constant<int, 1 % NS>{});
+        if (NS > 2) {
+            if (j0 + 2 >= n_tiles) break;
+            iteration(j0 + 2, std::integral_constant<int, 2 % NS>{});
+        }
+        if (NS > 3) {
+            if (j0 + 3 >= n_tiles) break;
+            iteration(j0 + 3, std::integral_constant<int, 3 % NS>{});
+        }
+    }
 
     wait_vmcnt<0>();   // no direct load may outlive the workgroup's LDS
 
     // ---- epilogue: divide by the row sum, round to bf16, store rows inside the question ----
-    const float l_tot = sum_halves(l_run);
+    const float l_tot = sum_halves(st.l);
     if (qrow >= L || row0 >= L) return;
     const float inv = 1.f / l_tot;
     uint16_t *op = static_cast<uint16_t *>(p.out) + ((int64_t)(a + qrow) * p.heads + head) * D;
@@ -245,41 +375,25 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
         for (int g4 = 0; g4 < 4; ++g4) {
             f32x4 f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) f[j] = o[db][g4 * 4 + j] * inv;
+            for (int jj = 0; jj < 4; ++jj) f[jj] = st.o[db][g4 * 4 + jj] * inv;
             *reinterpret_cast<bf16x4 *>(op + db * 32 + g4 * 8 + half * 4) = __builtin_convertvector(f, bf16x4);
         }
 }
 
-template <int D, int NW>
-hipError_t launch_nw(const PrefillArgs &a, int64_t grid, hipStream_t s) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, a);
-    return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_d(const PrefillArgs &a, int32_t waves, int64_t grid, hipStream_t s) {
-    switch (waves) {
-    case 1: return launch_nw<D, 1>(a, grid, s);
-    case 2: return launch_nw<D, 2>(a, grid, s);
-    case 3: return launch_nw<D, 3>(a, grid, s);
-    case 4: return launch_nw<D, 4>(a, grid, s);
-    case 5: return launch_nw<D, 5>(a, grid, s);
-    case 6: return launch_nw<D, 6>(a, grid, s);
-    case 7: return launch_nw<D, 7>(a, grid, s);
-    case 8: return launch_nw<D, 8>(a, grid, s);
-    default: return hipErrorInvalidValue;
-    }
-}
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int32_t waves,
-                               int64_t grid, hipStream_t s) {
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int64_t grid, hipStream_t s) {
     switch (head_dim) {
-    case 64: return launch_d<64>(a, waves, grid, s);
-    case 128: return launch_d<128>(a, waves, grid, s);
+    case 64:
+        hipLaunchKernelGGL((prefill_bf16_kernel<64>), dim3((unsigned)grid), dim3(NWAVE * 64), 0, s, a);
+        break;
+    case 128:
+        hipLaunchKernelGGL((prefill_bf16_kernel<128>), dim3((unsigned)grid), dim3(NWAVE * 64), 0, s, a);
+        break;
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
 }
 
 }  // namespace kev

@@ -8,11 +8,14 @@
 // blocks inside the item's own question at or left of its diagonal, so
 // cross-question and future tiles are never loaded.
 //
-// Order: query-block index t descending (cost t+1 key blocks, so the longest
-// items are issued first); within one t, questions come in descending length
-// order, ties in an unspecified order (an atomic counting sort).  The order
-// only decides which workgroup computes what: every item is computed the same
-// way wherever it runs, so outputs do not depend on it.
+// Order: question-major.  Questions come in descending number of query blocks
+// (ties in an unspecified order: an atomic counting sort), and the items of one
+// question with t descending (item t costs t+1 key blocks).  Workgroups that run
+// at the same time then mostly share one question's K/V rows, which stay in the
+// L2 of their XCD, the longest items of each question start first, and the
+// shortest questions come last.  The order only decides which workgroup
+// computes what: every item is computed the same way wherever it runs, so
+// outputs do not depend on it.
 #include "kev_internal.h"
 #include "../../include/kev.h"
 
@@ -57,8 +60,8 @@ constexpr int kLds = 2048;
 __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     __shared__ int32_t lds[kWaves];
     __shared__ int32_t s_bad, s_maxnb;
-    __shared__ int32_t t_cu[kLds + 1], t_hist[kLds], t_fill[kLds], t_cnt[kLds], t_start[kLds],
-        t_sigma[kLds];
+    __shared__ int32_t t_cu[kLds + 1], t_hist[kLds], t_fill[kLds], t_cnt[kLds], t_sigma[kLds],
+        t_qoff[kLds];
     const int tid = threadIdx.x;
     const ScheduleLayout lay = schedule_layout(a.n_seg, a.hist_len, 0);
     int32_t *ws = a.ws;
@@ -100,8 +103,8 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     int32_t *hist = small ? t_hist : ws + lay.hist;
     int32_t *fill = small ? t_fill : ws + lay.fill;
     int32_t *cnt = small ? t_cnt : ws + lay.cnt;
-    int32_t *start = small ? t_start : ws + lay.start;
     int32_t *sigma = small ? t_sigma : ws + lay.sigma;
+    int32_t *qoff = small ? t_qoff : ws + lay.qoff;
 
     for (int i = tid; i < maxnb + 2; i += kThreads) {
         hist[i] = 0;
@@ -122,17 +125,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     }
     if (tid == 0) cnt[maxnb] = 0;
     __syncthreads();
-
-    // start[e] = first position of level e (query block t = maxnb-1-e).
-    carry = 0;
-    for (int base = 0; base < maxnb; base += kThreads) {
-        int j = base + tid;
-        int32_t y = j < maxnb ? cnt[maxnb - 1 - j] : 0;
-        int32_t incl = block_scan(y, lds, &tot) + carry;
-        if (j < maxnb) start[j] = incl - y;
-        carry += tot;
-    }
-    const int32_t n_items = carry;
+    const int32_t n_q = maxnb > 0 ? cnt[0] : 0;   // questions with at least one block
 
     // sigma: questions in descending block count.
     for (int s = tid; s < a.n_seg; s += kThreads) {
@@ -141,16 +134,34 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     }
     __syncthreads();
 
-    // At level t the questions with more than t blocks are sigma[0 .. cnt[t]).
+    // qoff[r] = first item of the r-th question in that order.
+    carry = 0;
+    for (int base = 0; base < n_q; base += kThreads) {
+        int r = base + tid;
+        int32_t nb = 0;
+        if (r < n_q) {
+            const int32_t s = sigma[r];
+            nb = qblocks(cu[s + 1] - cu[s], br);
+        }
+        int32_t incl = block_scan(nb, lds, &tot) + carry;
+        if (r < n_q) qoff[r] = incl - nb;
+        carry += tot;
+    }
+    const int32_t n_items = carry;
+    __syncthreads();
+
+    // Item p belongs to the last question r with qoff[r] <= p; its t counts down from nb-1.
     for (int p = tid; p < n_items; p += kThreads) {
-        int lo = 0, hi = maxnb - 1;
+        int lo = 0, hi = n_q - 1;
         while (lo < hi) {
             int mid = (lo + hi + 1) >> 1;
-            if (start[mid] <= p) lo = mid;
+            if (qoff[mid] <= p) lo = mid;
             else hi = mid - 1;
         }
-        items[2 * p] = sigma[p - start[lo]];
-        items[2 * p + 1] = maxnb - 1 - lo;
+        const int32_t s = sigma[lo];
+        const int32_t nb = qblocks(cu[s + 1] - cu[s], br);
+        items[2 * p] = s;
+        items[2 * p + 1] = nb - 1 - (p - qoff[lo]);
     }
     if (tid == 0) ws[0] = n_items;
 }

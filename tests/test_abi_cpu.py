@@ -75,9 +75,11 @@ def test_decode_argument_checks(lib):
 
 
 def test_block_rows(lib):
-    assert K.kev_prefill_block_rows(28, 4, 128, K.KEV_BF16) == 32     # 7 heads x 1 row block
-    assert K.kev_prefill_block_rows(32, 8, 128, K.KEV_BF16) == 64     # 4 heads x 2 row blocks
-    assert K.kev_prefill_block_rows(4, 4, 128, K.KEV_BF16) == 128     # MHA: 4 row blocks
+    # items of 32*R rows with G*R a multiple of 4 (units fill 4-wavefront workgroups)
+    assert K.kev_prefill_block_rows(28, 4, 128, K.KEV_BF16) == 128    # G=7: R=4, 7 workgroups
+    assert K.kev_prefill_block_rows(32, 8, 128, K.KEV_BF16) == 32     # G=4: R=1, 1 workgroup
+    assert K.kev_prefill_block_rows(12, 2, 128, K.KEV_BF16) == 64     # G=6: R=2, 3 workgroups
+    assert K.kev_prefill_block_rows(4, 4, 128, K.KEV_BF16) == 128     # MHA: R=4
     assert K.kev_prefill_block_rows(4, 4, 16, K.KEV_F32) == 64
     assert K.kev_prefill_block_rows(4, 3, 128, K.KEV_BF16) == 0
 
@@ -114,8 +116,13 @@ def test_schedule_covers_each_unmasked_pair_once(block_rows):
         items = K.kev_schedule_host(cu, block_rows)
         assert len(items) == sum(-(-int(x) // block_rows) for x in lens)
         assert len({(int(s), int(t)) for s, t in items}) == len(items)
-        # heaviest first: query-block index never increases along the list
-        assert (np.diff(items[:, 1]) <= 0).all()
+        # question-major: questions in descending block count, t descending inside one
+        nb = np.array([-(-int(x) // block_rows) for x in lens])
+        assert (np.diff(nb[items[:, 0]]) <= 0).all()
+        same_q = items[1:, 0] == items[:-1, 0]
+        assert (items[1:, 1][same_q] == items[:-1, 1][same_q] - 1).all()
+        assert (items[1:, 1][~same_q] == nb[items[1:, 0][~same_q]] - 1).all()
+        assert items[0, 1] == nb[items[0, 0]] - 1
         seen = covered_pairs(items, cu, block_rows)
         expect = {(int(cu[s]) + i, int(cu[s]) + j) for s in range(len(lens))
                   for i in range(int(lens[s])) for j in range(i + 1)}
