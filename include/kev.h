@@ -147,21 +147,30 @@ int kev_get_device_errors(void *stream, int32_t *flags_out);
  * kev_prefill_block_rows: query rows per work item that a prefill call with
  * these arguments uses (0 if the combination is unsupported).
  *
+ * kev_prefill_order: the work-list order a prefill call with these arguments
+ * uses: KEV_ORDER_LEVEL (query block descending over all questions, so the
+ * longest items start first) when the K and V rows of one KV head take at most
+ * 8 MiB, else KEV_ORDER_QUESTION (question by question, longest question first,
+ * query block descending inside a question, so concurrently running workgroups
+ * share one question's rows in the L2 of their XCD).
+ *
  * kev_schedule_host: the work list computed on the host from a HOST copy of
- * cu_seqlens: items_out[2*i] = question, items_out[2*i+1] = query block, in
- * the order the device scheduler uses: question by question, questions in
- * descending number of query blocks (ties by index here, in an unspecified
- * order on the device), query block descending inside a question.  Returns
- * KEV_OK and *n_items_out, or KEV_ERR_INVALID_ARG if max_items is too small.
+ * cu_seqlens in the given order: items_out[2*i] = question, items_out[2*i+1] =
+ * query block.  Questions of equal block count come by index here and in an
+ * unspecified order on the device.  Returns KEV_OK and *n_items_out, or
+ * KEV_ERR_INVALID_ARG if max_items is too small or the order is unknown.
  *
  * kev_schedule_device: runs the device scheduler kernel on device cu_seqlens
  * and copies its work list to the host buffer items_out (synchronises).
  */
+#define KEV_ORDER_QUESTION 0
+#define KEV_ORDER_LEVEL 1
 int kev_prefill_block_rows(int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype);
+int kev_prefill_order(int32_t total_tokens, int32_t head_dim, int32_t dtype);
 int kev_schedule_host(const int32_t *cu_seqlens_host, int32_t n_seg, int32_t block_rows,
-                      int32_t *items_out, int32_t max_items, int32_t *n_items_out);
+                      int32_t order, int32_t *items_out, int32_t max_items, int32_t *n_items_out);
 int kev_schedule_device(const int32_t *cu_seqlens, int32_t n_seg, int32_t total_tokens,
-                        int32_t block_rows, int32_t *items_out, int32_t max_items,
+                        int32_t block_rows, int32_t order, int32_t *items_out, int32_t max_items,
                         int32_t *n_items_out, void *stream);
 
 #ifdef __cplusplus

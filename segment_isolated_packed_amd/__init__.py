@@ -24,6 +24,7 @@ KEV_ERR_BAD_SLOT = -5
 KEV_ERR_DEVICE = -6
 KEV_ERR_NO_MEMORY = -7
 KEV_DEVERR_SEQLENS, KEV_DEVERR_SLOT, KEV_DEVERR_CACHE_LEN = 1, 2, 4
+KEV_ORDER_QUESTION, KEV_ORDER_LEVEL = 0, 1
 
 
 class KevError(RuntimeError):
@@ -62,10 +63,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kev_status_string.restype = ctypes.c_char_p
     L.kev_get_device_errors.argtypes = [P, ctypes.POINTER(I)]
     L.kev_prefill_block_rows.argtypes = [I, I, I, I]
-    L.kev_schedule_host.argtypes = [P, I, I, P, I, ctypes.POINTER(I)]
-    L.kev_schedule_device.argtypes = [P, I, I, I, P, I, ctypes.POINTER(I), P]
+    L.kev_prefill_order.argtypes = [I, I, I]
+    L.kev_schedule_host.argtypes = [P, I, I, I, P, I, ctypes.POINTER(I)]
+    L.kev_schedule_device.argtypes = [P, I, I, I, I, P, I, ctypes.POINTER(I), P]
     for f in (L.kev_packed_attn_prefill, L.kev_slot_attn_decode, L.kev_get_device_errors,
-              L.kev_prefill_block_rows, L.kev_schedule_host, L.kev_schedule_device):
+              L.kev_prefill_block_rows, L.kev_prefill_order, L.kev_schedule_host,
+              L.kev_schedule_device):
         f.restype = ctypes.c_int
     _lib = L
     return L
@@ -178,7 +181,11 @@ def kev_prefill_block_rows(heads: int, kv_heads: int, head_dim: int, dtype: int)
     return int(load_library().kev_prefill_block_rows(heads, kv_heads, head_dim, dtype))
 
 
-def kev_schedule_host(cu_seqlens, block_rows: int):
+def kev_prefill_order(total_tokens: int, head_dim: int, dtype: int) -> int:
+    return int(load_library().kev_prefill_order(total_tokens, head_dim, dtype))
+
+
+def kev_schedule_host(cu_seqlens, block_rows: int, order: int = 0):
     """Work list (question, query block) computed on the host from a host copy of cu_seqlens."""
     import numpy as np
     L = load_library()
@@ -187,13 +194,13 @@ def kev_schedule_host(cu_seqlens, block_rows: int):
     cap = int(cu[-1]) // block_rows + n_seg + 1 if n_seg > 0 else 1
     items = np.zeros(2 * cap, dtype=np.int32)
     n = ctypes.c_int32(0)
-    _check(L.kev_schedule_host(cu.ctypes.data_as(ctypes.c_void_p), n_seg, block_rows,
+    _check(L.kev_schedule_host(cu.ctypes.data_as(ctypes.c_void_p), n_seg, block_rows, order,
                                items.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(n)),
            "kev_schedule_host")
     return items[: 2 * n.value].reshape(-1, 2)
 
 
-def kev_schedule_device(cu_seqlens, total_tokens: int, block_rows: int, stream=None):
+def kev_schedule_device(cu_seqlens, total_tokens: int, block_rows: int, order: int = 0, stream=None):
     """Work list produced by the device scheduler kernel (copied back; synchronises)."""
     import numpy as np
     L = load_library()
@@ -202,6 +209,6 @@ def kev_schedule_device(cu_seqlens, total_tokens: int, block_rows: int, stream=N
     items = np.zeros(2 * cap, dtype=np.int32)
     n = ctypes.c_int32(0)
     _check(L.kev_schedule_device(_dev_ptr(cu_seqlens, "cu_seqlens"), n_seg, total_tokens,
-                                 block_rows, items.ctypes.data_as(ctypes.c_void_p), cap,
+                                 block_rows, order, items.ctypes.data_as(ctypes.c_void_p), cap,
                                  ctypes.byref(n), _stream(stream)), "kev_schedule_device")
     return items[: 2 * n.value].reshape(-1, 2)

@@ -109,9 +109,19 @@ int host_check_seqlens(const int32_t *cu, int32_t n_seg, int32_t total_tokens) {
     return KEV_OK;
 }
 
+// Item order of a prefill call: level-major (longest items first overall) when the K and V
+// rows of one KV head take at most 8 MiB, i.e. fit the L2 caches of the XCDs serving that
+// head many times over; question-major otherwise, so concurrently running workgroups share
+// one question's rows.
+int32_t prefill_order(int32_t total_tokens, int32_t head_dim, int32_t dtype) {
+    if (dtype != KEV_BF16) return kOrderQuestion;
+    const int64_t kv_bytes = (int64_t)total_tokens * head_dim * 2 * 2;
+    return kv_bytes <= (int64_t(8) << 20) ? kOrderLevel : kOrderQuestion;
+}
+
 // Schedule on the device into the (device, stream) workspace.
 int run_schedule(const int32_t *cu, int32_t n_seg, int32_t total_tokens, int32_t block_rows,
-                 hipStream_t stream, int32_t **ws_out, ScheduleLayout *lay_out) {
+                 int32_t order, hipStream_t stream, int32_t **ws_out, ScheduleLayout *lay_out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
     int32_t *err = nullptr;
@@ -124,7 +134,7 @@ int run_schedule(const int32_t *cu, int32_t n_seg, int32_t total_tokens, int32_t
     void *ws = nullptr;
     rc = workspace(state().sched_ws, dev, stream, (size_t)lay.total * sizeof(int32_t), &ws);
     if (rc) return rc;
-    ScheduleArgs sa{cu, n_seg, total_tokens, block_rows, (int32_t)hist_len,
+    ScheduleArgs sa{cu, n_seg, total_tokens, block_rows, (int32_t)hist_len, order, n_max,
                     static_cast<int32_t *>(ws), err};
     rc = to_status(launch_schedule(sa, stream));
     if (rc) return rc;
@@ -183,7 +193,8 @@ int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
     const int32_t br = block_rows_for(heads, kv_heads, dtype);
     int32_t *ws = nullptr;
     ScheduleLayout lay;
-    int rc = run_schedule(cu_seqlens, n_seg, total_tokens, br, stream, &ws, &lay);
+    int rc = run_schedule(cu_seqlens, n_seg, total_tokens, br, prefill_order(total_tokens, head_dim, dtype),
+                          stream, &ws, &lay);
     if (rc) return rc;
     if (total_tokens == 0) return KEV_OK;   // only empty questions; cu_seqlens still checked
 
@@ -196,6 +207,7 @@ int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
     pa.cu = cu_seqlens;
     pa.sched = ws;
     pa.items_off = lay.items;
+    pa.rec = ws + lay.rec;
     pa.heads = heads;
     pa.kv_heads = kv_heads;
     pa.group = heads / kv_heads;
@@ -301,44 +313,61 @@ int kev_get_device_errors(void *stream_, int32_t *flags_out) {
     return KEV_OK;
 }
 
-int kev_schedule_host(const int32_t *cu, int32_t n_seg, int32_t block_rows, int32_t *items_out,
-                      int32_t max_items_, int32_t *n_items_out) {
+int kev_prefill_order(int32_t total_tokens, int32_t head_dim, int32_t dtype) {
+    return prefill_order(total_tokens, head_dim, dtype);
+}
+
+int kev_schedule_host(const int32_t *cu, int32_t n_seg, int32_t block_rows, int32_t order,
+                      int32_t *items_out, int32_t max_items_, int32_t *n_items_out) {
     if (!cu || n_seg < 0 || block_rows <= 0 || !n_items_out) return KEV_ERR_INVALID_ARG;
+    if (order != kOrderQuestion && order != kOrderLevel) return KEV_ERR_INVALID_ARG;
     if (n_seg == 0) {
         *n_items_out = 0;
         return KEV_OK;
     }
     int rc = host_check_seqlens(cu, n_seg, cu[n_seg]);
     if (rc) return rc;
-    std::vector<int32_t> nb(n_seg), order(n_seg);
+    std::vector<int32_t> nb(n_seg), qs(n_seg);   // qs: questions by descending block count
     int64_t total = 0;
     for (int32_t s = 0; s < n_seg; ++s) {
         nb[s] = qblocks(cu[s + 1] - cu[s], block_rows);
         total += nb[s];
-        order[s] = s;
+        qs[s] = s;
     }
     if (total > max_items_ || (total > 0 && !items_out)) return KEV_ERR_INVALID_ARG;
-    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return nb[x] > nb[y]; });
+    std::stable_sort(qs.begin(), qs.end(), [&](int32_t x, int32_t y) { return nb[x] > nb[y]; });
     int64_t p = 0;
-    for (int32_t i = 0; i < n_seg; ++i)
-        for (int32_t t = nb[order[i]] - 1; t >= 0; --t) {
-            items_out[2 * p] = order[i];
-            items_out[2 * p + 1] = t;
-            ++p;
-        }
+    if (order == kOrderLevel) {
+        int32_t maxnb = 0;
+        for (int32_t s = 0; s < n_seg; ++s) maxnb = std::max(maxnb, nb[s]);
+        for (int32_t t = maxnb - 1; t >= 0; --t)
+            for (int32_t i = 0; i < n_seg && nb[qs[i]] > t; ++i) {
+                items_out[2 * p] = qs[i];
+                items_out[2 * p + 1] = t;
+                ++p;
+            }
+    } else {
+        for (int32_t i = 0; i < n_seg; ++i)
+            for (int32_t t = nb[qs[i]] - 1; t >= 0; --t) {
+                items_out[2 * p] = qs[i];
+                items_out[2 * p + 1] = t;
+                ++p;
+            }
+    }
     *n_items_out = (int32_t)p;
     return KEV_OK;
 }
 
 int kev_schedule_device(const int32_t *cu_seqlens, int32_t n_seg, int32_t total_tokens,
-                        int32_t block_rows, int32_t *items_out, int32_t max_items_,
+                        int32_t block_rows, int32_t order, int32_t *items_out, int32_t max_items_,
                         int32_t *n_items_out, void *stream_) {
     if (!cu_seqlens || n_seg <= 0 || total_tokens < 0 || block_rows <= 0 || !n_items_out)
         return KEV_ERR_INVALID_ARG;
+    if (order != kOrderQuestion && order != kOrderLevel) return KEV_ERR_INVALID_ARG;
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     int32_t *ws = nullptr;
     ScheduleLayout lay;
-    int rc = run_schedule(cu_seqlens, n_seg, total_tokens, block_rows, stream, &ws, &lay);
+    int rc = run_schedule(cu_seqlens, n_seg, total_tokens, block_rows, order, stream, &ws, &lay);
     if (rc) return rc;
     int32_t n = 0;
     if (hipMemcpyAsync(&n, ws, sizeof n, hipMemcpyDeviceToHost, stream) != hipSuccess ||

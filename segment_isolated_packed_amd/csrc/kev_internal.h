@@ -56,25 +56,37 @@ struct ScheduleArgs {
     int32_t total_tokens;
     int32_t block_rows;
     int32_t hist_len;         // >= max query blocks per question + 2
+    int32_t order;            // kOrderQuestion or kOrderLevel
+    int64_t n_max_items;      // item capacity the workspace was laid out for
     int32_t *ws;              // workspace, see schedule_layout()
     int32_t *err;             // device error word
 };
 
+// Item orders.  Question-major: questions in descending length, query block t descending
+// inside a question (workgroups running together share one question's K/V rows).
+// Level-major: t descending over all questions, then descending length (longest items
+// first overall: the best balance when all K/V rows fit in the caches anyway).
+constexpr int32_t kOrderQuestion = 0;
+constexpr int32_t kOrderLevel = 1;
+
 // Workspace layout of the scheduler (int32 units):
-//   [0] n_items  [1] flags  [2..] hist[hist_len] | fill[hist_len] | cnt[hist_len] |
-//   sigma[n_seg] | qoff[n_seg] | items[2 * max_items]
+//   [0] n_items  [1..3] unused  [4..] hist[hist_len] | fill[hist_len] | cnt[hist_len] |
+//   start[hist_len] | sigma[n_seg] | qoff[n_seg] | items[2 * max_items] (question, t) |
+//   rec[4 * max_items] ({question start, question length, t, 0}, 16-byte aligned)
 struct ScheduleLayout {
-    int64_t hist, fill, cnt, sigma, qoff, items, total;
+    int64_t hist, fill, cnt, start, sigma, qoff, items, rec, total;
 };
 __host__ __device__ inline ScheduleLayout schedule_layout(int32_t n_seg, int32_t hist_len, int64_t n_max_items) {
     ScheduleLayout L;
     L.hist = 4;
     L.fill = L.hist + hist_len;
     L.cnt = L.fill + hist_len;
-    L.sigma = L.cnt + hist_len;
+    L.start = L.cnt + hist_len;
+    L.sigma = L.start + hist_len;
     L.qoff = L.sigma + n_seg;
     L.items = (L.qoff + n_seg + 3) & ~int64_t(3);
-    L.total = L.items + 2 * n_max_items;
+    L.rec = (L.items + 2 * n_max_items + 3) & ~int64_t(3);
+    L.total = L.rec + 4 * n_max_items;
     return L;
 }
 
@@ -84,6 +96,7 @@ struct PrefillArgs {
     const int32_t *cu;
     const int32_t *sched;     // scheduler workspace (n_items at [0], items at items_off)
     int64_t items_off;
+    const int32_t *rec;       // item records {question start, length, t, 0}
     int32_t heads, kv_heads, group;     // group = heads / kv_heads
     int32_t heads_per_wg, row_blocks, block_rows, n_hgroups;   // fp32 path
     int32_t wg_per_kvh;                 // bf16 path: workgroups per item and KV head

@@ -227,15 +227,16 @@ void prefill_bf16_kernel(PrefillArgs p) {
     auto kst = [&](int s) { return (lds_t *)smem + s * C::TB; };
     auto vst = [&](int s) { return (lds_t *)smem + (NS + s) * C::TB; };
 
-    const int32_t n_items = p.sched[0];
+    // The item record and the item count are read together (one round trip); records past
+    // the count exist (the record array covers the whole grid) and are not used.
     const int per_item = p.kv_heads * p.wg_per_kvh;
     const int item = blockIdx.x / per_item;
+    const __attribute__((address_space(4))) int *recs = (const __attribute__((address_space(4))) int *)p.rec;
+    const int a = recs[4 * item], L = recs[4 * item + 1], t = recs[4 * item + 2];
+    const int32_t n_items = ((const __attribute__((address_space(4))) int *)p.sched)[0];
     if (item >= n_items) return;
     const int rem = blockIdx.x - item * per_item;
     const int kvh = rem % p.kv_heads, w = rem / p.kv_heads;   // KV head fastest: see above
-    const int32_t *it = p.sched + p.items_off + 2 * item;
-    const int seg = it[0], t = it[1];
-    const int a = p.cu[seg], L = p.cu[seg + 1] - a;
     const int G = p.group;
 
     const int item_row0 = t * p.block_rows;
@@ -259,20 +260,7 @@ void prefill_bf16_kernel(PrefillArgs p) {
     const uint16_t *kg = static_cast<const uint16_t *>(p.k) + ((int64_t)a * p.kv_heads + kvh) * D;
     const uint16_t *vg = static_cast<const uint16_t *>(p.v) + ((int64_t)a * p.kv_heads + kvh) * D;
 
-    // Q^T operand: lane holds q row (row0 + col), d = dc*16 + half*8 .. +8.
     const int qrow = row0 + col;
-    bf16x8 qf[C::DC];
-    {
-        const uint16_t *qp = static_cast<const uint16_t *>(p.q) +
-                             ((int64_t)(a + qrow) * p.heads + head) * D + half * 8;
-#pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc) {
-            uint4 v4 = make_uint4(0, 0, 0, 0);
-            if (qrow < L) v4 = *reinterpret_cast<const uint4 *>(qp + dc * 16);
-            qf[dc] = __builtin_bit_cast(bf16x8, v4);
-        }
-    }
-    wait_vmcnt<0>();   // q is in registers before any direct load is in flight
 
     RowState<D> st;
 #pragma unroll
@@ -290,6 +278,19 @@ void prefill_bf16_kernel(PrefillArgs p) {
     auto kaddr = [&](int s) { return lds0 + (unsigned)(s * C::TB); };
     auto vaddr = [&](int s) { return lds0 + (unsigned)((NS + s) * C::TB); };
 
+    // Q^T operand: lane holds q row (row0 + col), d = dc*16 + half*8 .. +8; rows past the
+    // question read its last row (finite values in columns that are never stored).  Loaded
+    // with inline asm before the K/V prologue, so the one counted wait for K(0) below also
+    // covers these loads and no compiler wait drains the prologue.
+    bf16x8 qf[C::DC];
+    {
+        const uint16_t *qp = static_cast<const uint16_t *>(p.q) +
+                             ((int64_t)(a + min(qrow, L - 1)) * p.heads + head) * D + half * 8;
+#pragma unroll
+        for (int dc = 0; dc < C::DC; ++dc)
+            asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[dc]) : "v"(qp + dc * 16) : "memory");
+    }
+
     // Issue order: K(0); then, per (virtual) iteration i, K(i+NS) and V(i+NS-1).  At the
     // barrier of iteration j the wave needs K(j+1) and V(j), both issued at iteration
     // j-NS+1 with V last; the loads of at most NS-2 later iterations may stay in flight.
@@ -298,8 +299,10 @@ void prefill_bf16_kernel(PrefillArgs p) {
         if (i + NS < n_tiles) ld.issue(ld.kbase, i + NS, kaddr(i + NS), wave);
         if (i + NS - 1 < n_tiles) ld.issue(ld.vbase, i + NS - 1, vaddr(i + NS - 1), wave);
     }
-    if (n_tiles >= NS) wait_vmcnt<2 * C::NIT * (NS - 1)>();   // K(0) has landed
+    if (n_tiles >= NS) wait_vmcnt<2 * C::NIT * (NS - 1)>();   // q and K(0) have landed
     else wait_vmcnt<0>();
+    asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]));
+    if (C::DC > 4) asm volatile("" : "+v"(qf[4 % C::DC]), "+v"(qf[5 % C::DC]), "+v"(qf[6 % C::DC]), "+v"(qf[7 % C::DC]));
     barrier();
 
     bf16x8 kf[C::DC];             // K fragments of the next tile to score
@@ -365,10 +368,19 @@ void prefill_bf16_kernel(PrefillArgs p) {
     wait_vmcnt<0>();   // no direct load may outlive the workgroup's LDS
 
     // ---- epilogue: divide by the row sum, round to bf16, store rows inside the question ----
+    // A lane holds 4-element pieces of one row, so direct stores would touch 32 rows per
+    // instruction.  Each wavefront instead writes its 32 x D block to a free LDS stage (in
+    // the swizzled row layout) and stores whole rows from there: D/8 lanes per row, 16 B
+    // each.  Free stages: after the last barrier the other wavefronts read only K stage
+    // n_tiles % NS and V stage (n_tiles - 1) % NS, and no direct load is in flight, so
+    // wavefronts 0..2 take the other three K stages and wavefront 3 takes V stage
+    // n_tiles % NS.  LDS operations of one wavefront complete in order, so the reads see
+    // the writes without a barrier.
     const float l_tot = sum_halves(st.l);
-    if (qrow >= L || row0 >= L) return;
+    if (row0 >= L) return;
     const float inv = 1.f / l_tot;
-    uint16_t *op = static_cast<uint16_t *>(p.out) + ((int64_t)(a + qrow) * p.heads + head) * D;
+    using GM = Geom<D>;
+    lds_t *ob = wave < 3 ? kst((n_tiles + 1 + wave) % NS) : vst(n_tiles % NS);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -376,8 +388,19 @@ void prefill_bf16_kernel(PrefillArgs p) {
             f32x4 f;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) f[jj] = st.o[db][g4 * 4 + jj] * inv;
-            *reinterpret_cast<bf16x4 *>(op + db * 32 + g4 * 8 + half * 4) = __builtin_convertvector(f, bf16x4);
+            // row col, d = db*32 + g4*8 + half*4 .. +4: the half-chunk `half` of chunk db*4+g4
+            *reinterpret_cast<__attribute__((address_space(3))) bf16x4 *>(ob + GM::off(col, db * 4 + g4) + half * 8) =
+                __builtin_convertvector(f, bf16x4);
         }
+    const int rr = lane / GM::CPR, cc = lane % GM::CPR;
+    uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)(a + row0) * p.heads + head) * D + cc * 8;
+    const int64_t rstride = (int64_t)p.heads * D;
+#pragma unroll
+    for (int k = 0; k < 32 / GM::RPI; ++k) {
+        const int r = k * GM::RPI + rr;
+        const u32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(ob + GM::off(r, cc));
+        if (row0 + r < L) *reinterpret_cast<u32x4 *>(orow + r * rstride) = x;
+    }
 }
 
 

@@ -8,14 +8,15 @@
 // blocks inside the item's own question at or left of its diagonal, so
 // cross-question and future tiles are never loaded.
 //
-// Order: question-major.  Questions come in descending number of query blocks
-// (ties in an unspecified order: an atomic counting sort), and the items of one
-// question with t descending (item t costs t+1 key blocks).  Workgroups that run
-// at the same time then mostly share one question's K/V rows, which stay in the
-// L2 of their XCD, the longest items of each question start first, and the
-// shortest questions come last.  The order only decides which workgroup
-// computes what: every item is computed the same way wherever it runs, so
-// outputs do not depend on it.
+// Orders (item t costs t+1 key blocks; questions of equal block count come in an
+// unspecified order: an atomic counting sort):
+//  - question-major: questions in descending number of query blocks, the items of
+//    one question with t descending.  Workgroups that run at the same time then
+//    mostly share one question's K/V rows, which stay in the L2 of their XCD.
+//  - level-major: t descending over all questions, ties by descending length.  The
+//    longest items are issued first overall, the best balance of the two.
+// The order only decides which workgroup computes what: every item is computed the
+// same way wherever it runs, so outputs do not depend on it.
 #include "kev_internal.h"
 #include "../../include/kev.h"
 
@@ -60,12 +61,13 @@ constexpr int kLds = 2048;
 __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     __shared__ int32_t lds[kWaves];
     __shared__ int32_t s_bad, s_maxnb;
-    __shared__ int32_t t_cu[kLds + 1], t_hist[kLds], t_fill[kLds], t_cnt[kLds], t_sigma[kLds],
-        t_qoff[kLds];
+    __shared__ int32_t t_cu[kLds + 1], t_hist[kLds], t_fill[kLds], t_cnt[kLds], t_start[kLds],
+        t_sigma[kLds], t_qoff[kLds];
     const int tid = threadIdx.x;
-    const ScheduleLayout lay = schedule_layout(a.n_seg, a.hist_len, 0);
+    const ScheduleLayout lay = schedule_layout(a.n_seg, a.hist_len, a.n_max_items);
     int32_t *ws = a.ws;
     int32_t *items = ws + lay.items;
+    int4 *rec = reinterpret_cast<int4 *>(ws + lay.rec);
     const int32_t br = a.block_rows;
     const bool cu_small = a.n_seg + 1 <= kLds + 1;
 
@@ -103,6 +105,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     int32_t *hist = small ? t_hist : ws + lay.hist;
     int32_t *fill = small ? t_fill : ws + lay.fill;
     int32_t *cnt = small ? t_cnt : ws + lay.cnt;
+    int32_t *start = small ? t_start : ws + lay.start;
     int32_t *sigma = small ? t_sigma : ws + lay.sigma;
     int32_t *qoff = small ? t_qoff : ws + lay.qoff;
 
@@ -134,34 +137,63 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     }
     __syncthreads();
 
-    // qoff[r] = first item of the r-th question in that order.
-    carry = 0;
-    for (int base = 0; base < n_q; base += kThreads) {
-        int r = base + tid;
-        int32_t nb = 0;
-        if (r < n_q) {
-            const int32_t s = sigma[r];
-            nb = qblocks(cu[s + 1] - cu[s], br);
+    int32_t n_items;
+    if (a.order == kOrderLevel) {
+        // start[e] = first item of level e (query block t = maxnb-1-e), which holds the
+        // cnt[t] questions with more than t blocks: sigma[0 .. cnt[t]).
+        carry = 0;
+        for (int base = 0; base < maxnb; base += kThreads) {
+            const int e = base + tid;
+            const int32_t y = e < maxnb ? cnt[maxnb - 1 - e] : 0;
+            const int32_t incl = block_scan(y, lds, &tot) + carry;
+            if (e < maxnb) start[e] = incl - y;
+            carry += tot;
         }
-        int32_t incl = block_scan(nb, lds, &tot) + carry;
-        if (r < n_q) qoff[r] = incl - nb;
-        carry += tot;
-    }
-    const int32_t n_items = carry;
-    __syncthreads();
-
-    // Item p belongs to the last question r with qoff[r] <= p; its t counts down from nb-1.
-    for (int p = tid; p < n_items; p += kThreads) {
-        int lo = 0, hi = n_q - 1;
-        while (lo < hi) {
-            int mid = (lo + hi + 1) >> 1;
-            if (qoff[mid] <= p) lo = mid;
-            else hi = mid - 1;
+        n_items = carry;
+        __syncthreads();
+        for (int p = tid; p < n_items; p += kThreads) {
+            int lo = 0, hi = maxnb - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (start[mid] <= p) lo = mid;
+                else hi = mid - 1;
+            }
+            const int32_t s = sigma[p - start[lo]], t = maxnb - 1 - lo;
+            items[2 * p] = s;
+            items[2 * p + 1] = t;
+            rec[p] = make_int4(cu[s], cu[s + 1] - cu[s], t, 0);
         }
-        const int32_t s = sigma[lo];
-        const int32_t nb = qblocks(cu[s + 1] - cu[s], br);
-        items[2 * p] = s;
-        items[2 * p + 1] = nb - 1 - (p - qoff[lo]);
+    } else {
+        // qoff[r] = first item of the r-th question in that order.
+        carry = 0;
+        for (int base = 0; base < n_q; base += kThreads) {
+            const int r = base + tid;
+            int32_t nb = 0;
+            if (r < n_q) {
+                const int32_t s = sigma[r];
+                nb = qblocks(cu[s + 1] - cu[s], br);
+            }
+            const int32_t incl = block_scan(nb, lds, &tot) + carry;
+            if (r < n_q) qoff[r] = incl - nb;
+            carry += tot;
+        }
+        n_items = carry;
+        __syncthreads();
+        // Item p belongs to the last question r with qoff[r] <= p; its t counts down from nb-1.
+        for (int p = tid; p < n_items; p += kThreads) {
+            int lo = 0, hi = n_q - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (qoff[mid] <= p) lo = mid;
+                else hi = mid - 1;
+            }
+            const int32_t s = sigma[lo];
+            const int32_t nb = qblocks(cu[s + 1] - cu[s], br);
+            const int32_t t = nb - 1 - (p - qoff[lo]);
+            items[2 * p] = s;
+            items[2 * p + 1] = t;
+            rec[p] = make_int4(cu[s], cu[s + 1] - cu[s], t, 0);
+        }
     }
     if (tid == 0) ws[0] = n_items;
 }

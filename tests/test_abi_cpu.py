@@ -106,28 +106,46 @@ def covered_pairs(items, cu, block_rows):
     return seen
 
 
+@pytest.mark.parametrize("order", [0, 1])
 @pytest.mark.parametrize("block_rows", [32, 64, 128])
-def test_schedule_covers_each_unmasked_pair_once(block_rows):
-    rng = np.random.default_rng(block_rows)
+def test_schedule_covers_each_unmasked_pair_once(block_rows, order):
+    rng = np.random.default_rng(block_rows + 7 * order)
     for trial in range(4):
         lens = rng.integers(0, 300, size=int(rng.integers(1, 9)))
         lens[0] = max(lens[0], 1)
         cu = W.cu_from_lengths(lens)
-        items = K.kev_schedule_host(cu, block_rows)
+        items = K.kev_schedule_host(cu, block_rows, order)
         assert len(items) == sum(-(-int(x) // block_rows) for x in lens)
         assert len({(int(s), int(t)) for s, t in items}) == len(items)
-        # question-major: questions in descending block count, t descending inside one
         nb = np.array([-(-int(x) // block_rows) for x in lens])
-        assert (np.diff(nb[items[:, 0]]) <= 0).all()
-        same_q = items[1:, 0] == items[:-1, 0]
-        assert (items[1:, 1][same_q] == items[:-1, 1][same_q] - 1).all()
-        assert (items[1:, 1][~same_q] == nb[items[1:, 0][~same_q]] - 1).all()
-        assert items[0, 1] == nb[items[0, 0]] - 1
+        if order == K.KEV_ORDER_QUESTION:
+            # questions in descending block count, t descending inside one
+            assert (np.diff(nb[items[:, 0]]) <= 0).all()
+            same_q = items[1:, 0] == items[:-1, 0]
+            assert (items[1:, 1][same_q] == items[:-1, 1][same_q] - 1).all()
+            assert (items[1:, 1][~same_q] == nb[items[1:, 0][~same_q]] - 1).all()
+            assert items[0, 1] == nb[items[0, 0]] - 1
+        else:
+            # t never increases; inside one t, questions in descending block count
+            assert (np.diff(items[:, 1]) <= 0).all()
+            same_t = items[1:, 1] == items[:-1, 1]
+            assert (nb[items[1:, 0]][same_t] <= nb[items[:-1, 0]][same_t]).all()
         seen = covered_pairs(items, cu, block_rows)
         expect = {(int(cu[s]) + i, int(cu[s]) + j) for s in range(len(lens))
                   for i in range(int(lens[s])) for j in range(i + 1)}
         assert set(seen) == expect
         assert all(c == 1 for c in seen.values())
+
+
+def test_prefill_order_choice():
+    # level-major while one KV head's K and V rows take at most 8 MiB (bf16)
+    assert K.kev_prefill_order(9273, 128, K.KEV_BF16) == K.KEV_ORDER_LEVEL       # 4.7 MB
+    assert K.kev_prefill_order(16384, 128, K.KEV_BF16) == K.KEV_ORDER_LEVEL      # 8 MiB
+    assert K.kev_prefill_order(16385, 128, K.KEV_BF16) == K.KEV_ORDER_QUESTION
+    assert K.kev_prefill_order(131072, 128, K.KEV_BF16) == K.KEV_ORDER_QUESTION
+    assert K.kev_prefill_order(100, 16, K.KEV_F32) == K.KEV_ORDER_QUESTION
+    with pytest.raises(K.KevError):
+        K.kev_schedule_host(W.cu_from_lengths([5]), 32, 2)
 
 
 def test_skewed_long_visits_a_small_fraction_of_global_causal_tiles():

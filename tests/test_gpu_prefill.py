@@ -176,16 +176,17 @@ def test_device_schedule_matches_host_schedule():
         lens = W.prefill_lengths(name)
         cu = W.cu_from_lengths(lens)
         for br in (32, 64, 128):
-            say(f"schedule {name} block_rows={br}")
-            dev = K.kev_schedule_device(to_dev_i32(cu), int(cu[-1]), br)
-            host = K.kev_schedule_host(cu, br)
-            assert len(dev) == len(host)
-            # questions of equal block count may come in another order on the device:
-            # the (block count, query block) sequence and the item set must match
-            nb = -(-np.diff(cu) // br)
-            assert np.array_equal(nb[dev[:, 0]], nb[host[:, 0]])
-            assert np.array_equal(dev[:, 1], host[:, 1])
-            assert sorted(map(tuple, dev.tolist())) == sorted(map(tuple, host.tolist()))
+            for order in (K.KEV_ORDER_QUESTION, K.KEV_ORDER_LEVEL):
+                say(f"schedule {name} block_rows={br} order={order}")
+                dev = K.kev_schedule_device(to_dev_i32(cu), int(cu[-1]), br, order)
+                host = K.kev_schedule_host(cu, br, order)
+                assert len(dev) == len(host)
+                # questions of equal block count may come in another order on the device:
+                # the (block count, query block) sequence and the item set must match
+                nb = -(-np.diff(cu) // br)
+                assert np.array_equal(nb[dev[:, 0]], nb[host[:, 0]])
+                assert np.array_equal(dev[:, 1], host[:, 1])
+                assert sorted(map(tuple, dev.tolist())) == sorted(map(tuple, host.tolist()))
 
 
 def test_bad_cu_seqlens_flagged_and_nothing_written(monkeypatch):
