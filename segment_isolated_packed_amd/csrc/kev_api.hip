@@ -35,7 +35,6 @@ struct State {
     std::mutex mu;
     std::map<int, int32_t *> err_word;                        // device -> error word
     std::map<std::pair<int, void *>, Buffer> sched_ws;        // (device, stream)
-    std::map<std::pair<int, void *>, Buffer> decode_ws;       // (device, stream)
 };
 
 State &state() {
@@ -280,19 +279,9 @@ int kev_slot_attn_decode(const void *q, const kev_kv_pool *pool, const int32_t *
     da.group = heads / pool->kv_heads;
     da.n_slots = pool->n_slots;
     da.capacity = pool->capacity;
-    da.chunk = kDecodeChunk;
-    while ((pool->capacity + da.chunk - 1) / da.chunk > kDecodeMaxChunks) da.chunk *= 2;
-    da.max_chunks = (pool->capacity + da.chunk - 1) / da.chunk;
     da.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pool->head_dim));
     da.err = err;
-    const int64_t units = (int64_t)n_req * pool->kv_heads;
-    if (units * da.max_chunks > INT32_MAX) return KEV_ERR_INVALID_ARG;
-    const size_t partial_bytes =
-        (size_t)units * da.max_chunks * da.group * (pool->head_dim + 2) * sizeof(float);
-    void *ws = nullptr;
-    rc = workspace(state().decode_ws, dev, stream, partial_bytes, &ws);
-    if (rc) return rc;
-    da.partials = static_cast<float *>(ws);
+    if ((int64_t)n_req * pool->kv_heads > INT32_MAX) return KEV_ERR_INVALID_ARG;
     return to_status(launch_decode_bf16(da, pool->head_dim, stream));
 }
 

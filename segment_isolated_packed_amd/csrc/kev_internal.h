@@ -110,10 +110,7 @@ struct DecodeArgs {
     void *out;
     const void *k_new, *v_new;
     int32_t n_req, heads, kv_heads, group, n_slots, capacity;
-    int32_t chunk;            // positions per workgroup
-    int32_t max_chunks;       // ceil(capacity / chunk)
     float scale_log2;
-    float *partials;          // [n_req*kv_heads][max_chunks][group][head_dim + 2]
     int32_t *err;
 };
 
@@ -124,10 +121,5 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int64_t g
 hipError_t launch_prefill_f32(const PrefillArgs &a, int32_t head_dim, int64_t grid,
                               hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, int32_t head_dim, hipStream_t s);
-
-// Decode workgroup geometry.
-constexpr int32_t kDecodeWaves = 1;   // one wavefront per (request, KV head, chunk)
-constexpr int32_t kDecodeChunk = 256;      // positions per workgroup (doubled while a slot
-constexpr int32_t kDecodeMaxChunks = 16;   // would need more than kDecodeMaxChunks chunks)
 
 }  // namespace kev
