@@ -282,6 +282,12 @@ int kev_slot_attn_decode(const void *q, const kev_kv_pool *pool, const int32_t *
     da.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pool->head_dim));
     da.err = err;
     if ((int64_t)n_req * pool->kv_heads > INT32_MAX) return KEV_ERR_INVALID_ARG;
+    // Longest units first when the grid does not fit the CUs at once (two workgroups each);
+    // otherwise every workgroup starts at once and the order does not matter.
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return KEV_ERR_DEVICE;
+    da.ranked = (n_req <= 64 && (int64_t)n_req * pool->kv_heads > 2 * (int64_t)cus) ? 1 : 0;
     return to_status(launch_decode_bf16(da, pool->head_dim, stream));
 }
 

@@ -29,8 +29,9 @@
 //     section 2.4) within each wavefront; the four partial states are merged
 //     in LDS with the same rescaling identity, so a call is one kernel with
 //     no global partials;
-//   - workgroups are issued longest unit first (for up to 64 requests), so the
-//     short units fill in at the end.
+//   - when there are more units than the CUs hold at once (and at most 64
+//     requests), workgroups are issued longest unit first, so the short units
+//     fill in at the end.
 #include "kev_internal.h"
 #include "kev_mfma_core.h"
 #include "../../include/kev.h"
@@ -48,15 +49,19 @@ __device__ inline bool req_valid(int slot, int L, const DecodeArgs &p) {
     return slot >= 0 && slot < p.n_slots && L >= 1 && L <= p.capacity;
 }
 
-// Request handled by the workgroups of rank b_req: requests ordered by tile count,
-// descending (ties by index), when there are at most 64 of them; index order otherwise.
-__device__ inline int pick_request(int b_req, const DecodeArgs &p) {
-    if (p.n_req > 64) return b_req;
+// Request, slot and length for the workgroups of rank b_req: requests ordered by tile count,
+// descending (ties by index).  Used when there are at most 64 requests and more units than
+// the CUs hold at once, so that short units fill in at the end.
+struct Req {
+    int r, slot, L;
+};
+__device__ inline Req ranked_request(int b_req, const DecodeArgs &p) {
     const int lane = threadIdx.x & 63;
-    int t = -1;
+    int t = -1, sl = 0, ln = 0;
     if (lane < p.n_req) {
-        const int s = p.slot_ids[lane], L = p.cache_lens[lane];
-        t = req_valid(s, L, p) ? (L + DKT - 1) / DKT : 0;
+        sl = p.slot_ids[lane];
+        ln = p.cache_lens[lane];
+        t = req_valid(sl, ln, p) ? (ln + DKT - 1) / DKT : 0;
     }
     int rank = 0;
     for (int j = 0; j < p.n_req; ++j) {
@@ -64,7 +69,8 @@ __device__ inline int pick_request(int b_req, const DecodeArgs &p) {
         rank += (tj > t || (tj == t && j < lane)) ? 1 : 0;
     }
     const uint64_t hit = __ballot(lane < p.n_req && rank == b_req);
-    return hit ? (int)__builtin_ctzll(hit) : b_req;
+    const int f = hit ? (int)__builtin_ctzll(hit) : 0;   // ranks are a permutation: always hit
+    return Req{f, __builtin_amdgcn_readlane(sl, f), __builtin_amdgcn_readlane(ln, f)};
 }
 
 template <int D>
@@ -82,10 +88,18 @@ void decode_bf16_kernel(DecodeArgs p) {
     const int lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
     const int G = p.group, KVH = p.kv_heads;
-    const int r = __builtin_amdgcn_readfirstlane(pick_request(blockIdx.x / KVH, p));
     const int g = blockIdx.x % KVH;
-    const int slot = p.slot_ids[r];
-    const int L = p.cache_lens[r];
+    int r, slot, L;
+    if (p.ranked) {
+        const Req q = ranked_request(blockIdx.x / KVH, p);
+        r = q.r;
+        slot = q.slot;
+        L = q.L;
+    } else {
+        r = blockIdx.x / KVH;
+        slot = p.slot_ids[r];
+        L = p.cache_lens[r];
+    }
     if (!req_valid(slot, L, p)) {
         if (g == 0 && threadIdx.x == 0)
             atomicOr(p.err, (int32_t)((slot < 0 || slot >= p.n_slots) ? KEV_DEVERR_SLOT : KEV_DEVERR_CACHE_LEN));

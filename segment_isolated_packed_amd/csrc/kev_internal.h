@@ -110,6 +110,7 @@ struct DecodeArgs {
     void *out;
     const void *k_new, *v_new;
     int32_t n_req, heads, kv_heads, group, n_slots, capacity;
+    int32_t ranked;           // 1: workgroups take units longest first (n_req <= 64)
     float scale_log2;
     int32_t *err;
 };

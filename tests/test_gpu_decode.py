@@ -55,6 +55,20 @@ def test_head_layouts_and_edges(orc, hq, hk, d):
     assert np.array_equal(to_host_bits(pool), ref_pool)
 
 
+@pytest.mark.parametrize("n_req,hq,hk,d", [(48, 32, 16, 64), (80, 16, 8, 128)])
+def test_many_units_grid_orders(orc, n_req, hq, hk, d):
+    # more (request, KV head) units than two per CU: 48 requests are issued longest first,
+    # 80 requests (over 64) in index order
+    dc = W.make_decode(n_req=n_req, n_slots=n_req + 3, capacity=300, heads=hq, kv_heads=hk,
+                       head_dim=d, seed=n_req + hk)
+    say(f"decode {n_req} req {hq}/{hk} d{d}")
+    out, pool = run(dc)
+    assert K.kev_get_device_errors() == 0
+    ref, ref_pool = orc.decode_case(dc, want_pool=True)
+    assert_parity(to_host_f64(out), ref, dc.dtype, f"decode {n_req} req {hq}/{hk} d{d}")
+    assert np.array_equal(to_host_bits(pool), ref_pool)
+
+
 def test_length_one_returns_v_new_exactly():
     dc = W.make_decode(n_req=3, n_slots=4, capacity=64, heads=8, kv_heads=2, head_dim=128,
                        seed=3, cache_lens=[1, 1, 1])
