@@ -225,6 +225,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": gbps / PEAK_HBM_GBPS if gbps else None,
                          "traffic": traffic_for("decode_bf16_kernel", dec_hash),
+                         "kernel": "kev decode_bf16_kernel<128> (one decode call, the only kernel)",
                          "algorithmic_bytes_per_launch": dbytes},
         },
         "cpu_baseline": None,

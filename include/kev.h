@@ -148,11 +148,11 @@ int kev_get_device_errors(void *stream, int32_t *flags_out);
  * these arguments uses (0 if the combination is unsupported).
  *
  * kev_prefill_order: the work-list order a prefill call with these arguments
- * uses: KEV_ORDER_LEVEL (query block descending over all questions, so the
- * longest items start first) when the K and V rows of one KV head take at most
- * 8 MiB, else KEV_ORDER_QUESTION (question by question, longest question first,
- * query block descending inside a question, so concurrently running workgroups
- * share one question's rows in the L2 of their XCD).
+ * uses.  Currently always KEV_ORDER_QUESTION (question by question, longest
+ * question first, query block descending inside a question, so concurrently
+ * running workgroups share one question's rows in the L2 of their XCD).
+ * KEV_ORDER_LEVEL (query block descending over all questions, longest items
+ * first overall) is available to the schedule entry points below.
  *
  * kev_schedule_host: the work list computed on the host from a HOST copy of
  * cu_seqlens in the given order: items_out[2*i] = question, items_out[2*i+1] =

@@ -198,10 +198,72 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     if (tid == 0) ws[0] = n_items;
 }
 
+// The same work list for at most 64 questions, built by one wavefront with every question
+// in a lane: no LDS tables and no workgroup barriers, so the pass costs little more than one
+// read of cu_seqlens and the stores of the list.  Ties in block count go by question index.
+__global__ __launch_bounds__(64) void schedule_small_kernel(ScheduleArgs a) {
+    const ScheduleLayout lay = schedule_layout(a.n_seg, a.hist_len, a.n_max_items);
+    int32_t *ws = a.ws;
+    int32_t *items = ws + lay.items;
+    int4 *rec = reinterpret_cast<int4 *>(ws + lay.rec);
+    const int lane = threadIdx.x;
+    int q0 = 0, len = 0;
+    if (lane < a.n_seg) {
+        q0 = a.cu[lane];
+        len = a.cu[lane + 1] - q0;
+    }
+    const int nb = lane < a.n_seg ? qblocks(len, a.block_rows) : 0;
+    const bool bad = __any(len < 0 || nb + 1 >= a.hist_len) || a.cu[0] != 0 || a.cu[a.n_seg] != a.total_tokens;
+    if (bad) {
+        if (lane == 0) {
+            ws[0] = 0;
+            atomicOr(a.err, (int32_t)KEV_DEVERR_SEQLENS);
+        }
+        return;
+    }
+    // rank: position in descending block count (ties by index); before: items of the questions
+    // ranked ahead (question-major offset of this question's first item)
+    int rank = 0, before = 0, maxnb = 0;
+    for (int j = 0; j < a.n_seg; ++j) {
+        const int nj = __builtin_amdgcn_readlane(nb, j);
+        const bool ahead = nj > nb || (nj == nb && j < lane);
+        rank += ahead ? 1 : 0;
+        before += ahead ? nj : 0;
+        maxnb = max(maxnb, nj);
+    }
+    int n_items = 0;
+    for (int j = 0; j < a.n_seg; ++j) n_items += __builtin_amdgcn_readlane(nb, j);
+    if (a.order == kOrderLevel) {
+        // level t holds the questions with more than t blocks, in rank order; levels go
+        // from t = maxnb-1 down, so item (q, t) sits after every item of the levels above
+        int above = 0;   // items in levels t' > t
+        for (int t = maxnb - 1; t >= 0; --t) {
+            if (nb > t) {
+                const int p = above + rank;
+                items[2 * p] = lane;
+                items[2 * p + 1] = t;
+                rec[p] = make_int4(q0, len, t, 0);
+            }
+            int c = 0;
+            for (int j = 0; j < a.n_seg; ++j) c += __builtin_amdgcn_readlane(nb, j) > t ? 1 : 0;
+            above += c;
+        }
+    } else {
+        for (int k = 0; k < nb; ++k) {
+            const int p = before + k, t = nb - 1 - k;
+            items[2 * p] = lane;
+            items[2 * p + 1] = t;
+            rec[p] = make_int4(q0, len, t, 0);
+        }
+    }
+    if (lane == 0) ws[0] = n_items;
+}
+
 }  // namespace
 
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), 0, s, a);
+    if (a.n_seg <= 64) hipLaunchKernelGGL(schedule_small_kernel, dim3(1), dim3(64), 0, s, a);
+    else hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

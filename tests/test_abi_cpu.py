@@ -138,12 +138,9 @@ def test_schedule_covers_each_unmasked_pair_once(block_rows, order):
 
 
 def test_prefill_order_choice():
-    # level-major while one KV head's K and V rows take at most 8 MiB (bf16)
-    assert K.kev_prefill_order(9273, 128, K.KEV_BF16) == K.KEV_ORDER_LEVEL       # 4.7 MB
-    assert K.kev_prefill_order(16384, 128, K.KEV_BF16) == K.KEV_ORDER_LEVEL      # 8 MiB
-    assert K.kev_prefill_order(16385, 128, K.KEV_BF16) == K.KEV_ORDER_QUESTION
-    assert K.kev_prefill_order(131072, 128, K.KEV_BF16) == K.KEV_ORDER_QUESTION
-    assert K.kev_prefill_order(100, 16, K.KEV_F32) == K.KEV_ORDER_QUESTION
+    # prefill calls use the question-major order whatever the size and dtype
+    for tokens, d, dt in ((9273, 128, K.KEV_BF16), (131072, 128, K.KEV_BF16), (100, 16, K.KEV_F32)):
+        assert K.kev_prefill_order(tokens, d, dt) == K.KEV_ORDER_QUESTION
     with pytest.raises(K.KevError):
         K.kev_schedule_host(W.cu_from_lengths([5]), 32, 2)
 

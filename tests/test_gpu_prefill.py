@@ -83,7 +83,11 @@ def test_fp32_head_dims(orc, d):
 
 
 @pytest.mark.parametrize("lens", [[1], [1] * 50, [2048], [33, 31, 32, 65, 63, 64, 127, 129],
-                                  [0, 0, 5, 0], [4097, 3]])
+                                  [0, 0, 5, 0], [4097, 3],
+                                  # 64 questions (items derived in the attention kernel) and 65
+                                  # (scheduling pass first), equal and mixed lengths
+                                  [3] * 64, [3] * 65, [(i * 37) % 90 for i in range(64)],
+                                  [(i * 37) % 90 for i in range(65)]])
 def test_segment_edge_cases(orc, lens):
     check_full(W.make_prefill(lens, 8, 2, 128, W.BF16, seed=len(lens)), orc, f"bf16 lens={lens[:8]}")
 
@@ -205,3 +209,9 @@ def test_bad_cu_seqlens_flagged_and_nothing_written(monkeypatch):
     with pytest.raises(K.KevError) as e:
         K.kev_packed_attn_prefill(q, k, k, to_dev_i32([0, 4, 9]), out=out)   # ends short of T
     assert e.value.code == K.KEV_ERR_BAD_SEQLENS
+    monkeypatch.delenv("KEV_CHECK")
+    for bad in ([0, 4, 9], [1, 4, 10], [0] + [5] * 35 + [3] * 35 + [10]):   # short end, nonzero start, 71 segs
+        say(f"prefill bad cu_seqlens {bad[:4]}.. (device check, {len(bad) - 1} segments)")
+        K.kev_packed_attn_prefill(q, k, k, to_dev_i32(bad), out=out)
+        assert K.kev_get_device_errors() & K.KEV_DEVERR_SEQLENS
+        assert bool((out == 7.0).all())
