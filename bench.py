@@ -217,7 +217,7 @@ def main():
             "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / PEAK_BF16_TFLOPS if tflops else None,
             "traffic": traffic_for("prefill_bf16_kernel", pre_hash),
-            "kernel": "kev schedule_kernel + prefill_bf16_kernel<128> (one prefill call)",
+            "kernel": "kev schedule_small_kernel + prefill_bf16_kernel<128> (one prefill call, both launches)",
             "algorithmic_flops_per_launch": flops,
         },
         "decode": {
