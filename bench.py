@@ -176,6 +176,29 @@ def main():
     wall = time.perf_counter() - t0
     log("timed region done")
 
+    # Prefill-to-slot handoff (kev_packed_attn_prefill_slots) on the same workload: every
+    # question's K/V rows stored into its own slot of a pool sized for its longest question.
+    slots_res = None
+    if do_pre and pc.dtype == W.BF16:
+        cap = int(max(pc.seqlens.max(), 1))
+        spool = torch.zeros((pc.n_seg + 4, 2, pc.kv_heads, cap, pc.head_dim), dtype=torch.bfloat16, device=dev)
+        sids = torch.arange(pc.n_seg, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            K.kev_packed_attn_prefill_slots(q, k, v, cu, spool, sids, out=out)
+        torch.cuda.synchronize()
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in sev:
+            e[0].record(stream)
+            K.kev_packed_attn_prefill_slots(q, k, v, cu, spool, sids, out=out)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        if K.kev_get_device_errors():
+            raise RuntimeError("device error flags in the prefill-to-slot leg")
+        slots_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in sev]))
+        store_bytes = 2 * 2 * pc.total_tokens * pc.kv_heads * pc.head_dim * 2   # K and V, read + write
+        slots_res = {"ms": slots_ms, "store_bytes": store_bytes, "slot_capacity": cap}
+        del spool
+
     pre_ms = [e[0].elapsed_time(e[1]) for e in events] if do_pre else [float("nan")]
     dec_ms = [e[2].elapsed_time(e[3]) for e in events] if do_dec else [float("nan")]
     pre_avg = float(np.mean(pre_ms))
@@ -228,6 +251,11 @@ def main():
                          "kernel": "kev decode_bf16_kernel<128> (one decode call, the only kernel)",
                          "algorithmic_bytes_per_launch": dbytes},
         },
+        "prefill_slots": None if slots_res is None else {
+            "ms": slots_res["ms"], "extra_ms_vs_prefill": slots_res["ms"] - pre_avg,
+            "store_bytes": slots_res["store_bytes"], "slot_capacity": slots_res["slot_capacity"],
+            "store_gbps_incl_launch": slots_res["store_bytes"] / max(slots_res["ms"] - pre_avg, 1e-6) / 1e6,
+            "call": "kev_packed_attn_prefill_slots: prefill + every question's K/V stored into its slot"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and do_pre:

@@ -21,6 +21,9 @@
  *       in place, not concatenated (primer, section 2.2), and the new query
  *       attends over all cached positions with no mask (same section).
  *
+ *   kev_packed_attn_prefill_slots  the prefill, and each question's K/V rows
+ *       stored into its slot of that pool (the handoff to decode).
+ *
  * Conventions shared by every call
  *   - Tensor pointers are DEVICE pointers owned by the caller, contiguous in
  *     the layouts stated below, never freed or retained by the library.
@@ -131,6 +134,31 @@ int kev_slot_attn_decode(const void *q, const kev_kv_pool *kv_pool,
                          const int32_t *slot_ids, const int32_t *cache_lens, void *out,
                          const void *k_new, const void *v_new, int32_t n_req, int32_t heads,
                          void *stream);
+
+/*
+ * Packed prefill that also hands each question its slot: the prefill above,
+ * then question s's K and V rows become rows 0..len_s-1 of slot slot_ids[s]
+ * (every KV head, K and V planes), written in place -- each question gets a
+ * slot on entry and decode continues it there (Kev part 2, gsyq.cn, section
+ * 2.2; primer, sakurs2.com, section 2.2).  A following kev_slot_attn_decode
+ * with cache_lens[r] = len_s + 1 appends the question's next token.
+ *
+ *   q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out, total_tokens:
+ *                as for kev_packed_attn_prefill (bf16 only)
+ *   kv_pool      host pointer to the pool descriptor; kv_heads and head_dim
+ *                must equal the call's, dtype KEV_BF16
+ *   slot_ids     int32 [n_seg], device; distinct slots in [0, n_slots)
+ *
+ * Rows len_s .. capacity-1 of a slot and all other slots are not written.
+ * A question longer than the capacity, or with an out-of-range slot id, is
+ * not stored (KEV_DEVERR_CACHE_LEN / KEV_DEVERR_SLOT in the device error
+ * word; KEV_ERR_SLOT_OVERFLOW / KEV_ERR_BAD_SLOT under KEV_CHECK=1, which also
+ * rejects repeated slot ids); its attention output is still computed.
+ */
+int kev_packed_attn_prefill_slots(const void *q, const void *k, const void *v,
+                                  const int32_t *cu_seqlens, int32_t n_seg, int32_t heads,
+                                  int32_t kv_heads, int32_t head_dim, void *out, int32_t total_tokens,
+                                  const kev_kv_pool *kv_pool, const int32_t *slot_ids, void *stream);
 
 /* Human-readable text for a kev_status value (static storage). */
 const char *kev_status_string(int status);

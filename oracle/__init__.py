@@ -5,7 +5,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 its binding, and the HIP path never imports it.
 
 ``kev_oracle.c`` holds the plain fp64 loops (full prefill, sampled prefill
-rows, slot-pool decode); ``dense.py`` holds the explicit dense-mask brute
+rows, slot-pool decode) and the prefill-to-slot K/V store; ``dense.py`` holds the explicit dense-mask brute
 force for tiny inputs.  Each function cites the passage of the pages it
 follows in its own header comment or docstring.
 """
@@ -73,9 +73,10 @@ class Oracle:
         L.kev_oracle_prefill.argtypes = [P, P, P, C, P, I, I, I, I, P, C]
         L.kev_oracle_prefill_rows.argtypes = [P, P, P, C, P, I, I, I, I, P, P, I, P, C]
         L.kev_oracle_decode.argtypes = [P, P, I, I, I, I, P, P, P, P, I, I, C, P, P, C]
+        L.kev_oracle_store_kv.argtypes = [P, P, C, P, I, I, I, P, P, I, I, P]
         L.kev_oracle_max_threads.argtypes = []
         for f in (L.kev_oracle_prefill, L.kev_oracle_prefill_rows, L.kev_oracle_decode,
-                  L.kev_oracle_max_threads):
+                  L.kev_oracle_store_kv, L.kev_oracle_max_threads):
             f.restype = C
         self._L = L
         self.path = path
@@ -135,6 +136,23 @@ class Oracle:
             _ptr(cache_lens), _ptr(k_new), _ptr(v_new), n_req, heads, _code(dtype), _ptr(out),
             _ptr(after), n_threads))
         return (out, after) if want_pool else out
+
+    def store_kv(self, k, v, cu_seqlens, slot_ids, pool, dtype: str) -> np.ndarray:
+        """Prefill-to-slot handoff: the pool after question s's K/V rows become rows
+        0..len-1 of slot slot_ids[s] (every other byte unchanged)."""
+        k, v, pool = (_input(x, dtype) for x in (k, v, pool))
+        n_slots, two, kv_heads, capacity, d = pool.shape
+        if two != 2:
+            raise ValueError("pool must be [n_slots, 2, kv_heads, capacity, d]")
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        slot_ids = np.ascontiguousarray(slot_ids, dtype=np.int32)
+        if len(slot_ids) != len(cu) - 1 or k.shape[0] != (int(cu[-1]) if len(cu) else 0):
+            raise OracleError(-1)
+        after = np.empty_like(pool)
+        self._check(self._L.kev_oracle_store_kv(_ptr(k), _ptr(v), _code(dtype), _ptr(cu), len(cu) - 1,
+                                                kv_heads, d, _ptr(slot_ids), _ptr(pool), n_slots,
+                                                capacity, _ptr(after)))
+        return after
 
     def decode_case(self, case, want_pool: bool = False, n_threads: int = 0):
         return self.decode(case.q, case.pool, case.slot_ids, case.cache_lens, case.k_new,

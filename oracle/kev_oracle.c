@@ -388,3 +388,49 @@ int kev_oracle_decode(const void *q, const void *pool, int32_t n_slots, int32_t 
     }
     return ORACLE_OK;
 }
+
+/*
+ * Prefill-to-slot handoff: question s of a packed prefill gets slot slot_ids[s]
+ * on entry, and its K/V rows become rows 0..len-1 of that slot, written in
+ * place (Kev part 2, gsyq.cn, section 2.2: one slot per question, assigned on
+ * entry; primer, sakurs2.com, section 2.2: the cache is pre-allocated space
+ * written in place, not concatenated).
+ *   k/v[T, kv_heads, d] with T = cu[n_seg]; pool[n_slots][2][kv_heads][capacity][d].
+ *   pool_after receives a copy of the pool with those rows replaced; every
+ *   other row keeps its bytes.
+ */
+int kev_oracle_store_kv(const void *k, const void *v, int dtype, const int32_t *cu,
+                        int32_t n_seg, int32_t kv_heads, int32_t d, const int32_t *slot_ids,
+                        const void *pool, int32_t n_slots, int32_t capacity, void *pool_after)
+{
+    int rc = check_seqlens(cu, n_seg);
+    if (rc)
+        return rc;
+    if (kv_heads <= 0 || d <= 0 || n_slots <= 0 || capacity <= 0 ||
+        (dtype != ORACLE_BF16 && dtype != ORACLE_F32))
+        return ORACLE_BAD_ARG;
+    for (int32_t s = 0; s < n_seg; s++) {
+        if (slot_ids[s] < 0 || slot_ids[s] >= n_slots)
+            return ORACLE_BAD_SLOT;
+        if (cu[s + 1] - cu[s] > capacity)
+            return ORACLE_SLOT_OVERFLOW;
+        for (int32_t s2 = 0; s2 < s; s2++)
+            if (slot_ids[s2] == slot_ids[s])
+                return ORACLE_BAD_SLOT;
+    }
+    size_t esz = dtype == ORACLE_F32 ? 4 : 2;
+    size_t plane = (size_t)capacity * d;
+    size_t slot_elems = (size_t)2 * kv_heads * plane;
+    memcpy(pool_after, pool, esz * slot_elems * (size_t)n_slots);
+    for (int32_t s = 0; s < n_seg; s++)
+        for (int32_t i = cu[s]; i < cu[s + 1]; i++)
+            for (int32_t g = 0; g < kv_heads; g++) {
+                size_t kdst = (size_t)slot_ids[s] * slot_elems + (size_t)g * plane +
+                              (size_t)(i - cu[s]) * d;
+                size_t vdst = kdst + (size_t)kv_heads * plane;
+                size_t src = ((size_t)i * kv_heads + g) * d;
+                memcpy((char *)pool_after + kdst * esz, (const char *)k + src * esz, esz * d);
+                memcpy((char *)pool_after + vdst * esz, (const char *)v + src * esz, esz * d);
+            }
+    return ORACLE_OK;
+}

@@ -59,6 +59,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I = ctypes.c_void_p, ctypes.c_int32
     L.kev_packed_attn_prefill.argtypes = [P, P, P, P, I, I, I, I, P, I, I, P]
     L.kev_slot_attn_decode.argtypes = [P, ctypes.POINTER(KvPool), P, P, P, P, P, I, I, P]
+    L.kev_packed_attn_prefill_slots.argtypes = [P, P, P, P, I, I, I, I, P, I, ctypes.POINTER(KvPool), P, P]
     L.kev_status_string.argtypes = [ctypes.c_int]
     L.kev_status_string.restype = ctypes.c_char_p
     L.kev_get_device_errors.argtypes = [P, ctypes.POINTER(I)]
@@ -66,7 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kev_prefill_order.argtypes = [I, I, I]
     L.kev_schedule_host.argtypes = [P, I, I, I, P, I, ctypes.POINTER(I)]
     L.kev_schedule_device.argtypes = [P, I, I, I, I, P, I, ctypes.POINTER(I), P]
-    for f in (L.kev_packed_attn_prefill, L.kev_slot_attn_decode, L.kev_get_device_errors,
+    for f in (L.kev_packed_attn_prefill, L.kev_slot_attn_decode, L.kev_packed_attn_prefill_slots,
+              L.kev_get_device_errors,
               L.kev_prefill_block_rows, L.kev_prefill_order, L.kev_schedule_host,
               L.kev_schedule_device):
         f.restype = ctypes.c_int
@@ -166,6 +168,47 @@ def kev_slot_attn_decode(q, kv_pool, slot_ids, cache_lens, k_new, v_new, out=Non
                                 _dev_ptr(out, "out"), _dev_ptr(k_new, "k_new"),
                                 _dev_ptr(v_new, "v_new"), n_req, heads, _stream(stream))
     _check(rc, "kev_slot_attn_decode")
+    return out
+
+
+def kev_packed_attn_prefill_slots(q, k, v, cu_seqlens, kv_pool, slot_ids, out=None,
+                                  total_tokens: int | None = None, stream=None):
+    """Packed prefill that also stores question s's K/V rows as rows 0..len-1 of slot
+    slot_ids[s] of kv_pool (bf16, [n_slots, 2, kv_heads, capacity, d], updated in place).
+
+    q [T, heads, d], k/v [T, kv_heads, d] (bf16), cu_seqlens / slot_ids int32 on the device.
+    Returns out [T, heads, d].
+    """
+    import torch
+    L = load_library()
+    T, heads, d = q.shape
+    kv_heads = k.shape[1]
+    if k.shape != (T, kv_heads, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [T, kv_heads, head_dim] matching q")
+    n_slots, two, pkvh, capacity, pd = kv_pool.shape
+    if two != 2 or pd != d or pkvh != kv_heads:
+        raise ValueError("kv_pool must be [n_slots, 2, kv_heads, capacity, head_dim] matching k")
+    for t in (k, v, kv_pool):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, kv_pool must share one dtype")
+    for name, t in (("cu_seqlens", cu_seqlens), ("slot_ids", slot_ids)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    n_seg = cu_seqlens.numel() - 1
+    if slot_ids.numel() != n_seg:
+        raise ValueError("slot_ids must have one entry per question")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    pool = KvPool(_dev_ptr(kv_pool, "kv_pool").value, n_slots, capacity, kv_heads, d,
+                  _dtype_code(kv_pool))
+    rc = L.kev_packed_attn_prefill_slots(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                         _dev_ptr(cu_seqlens, "cu_seqlens"), n_seg, heads, kv_heads,
+                                         d, _dev_ptr(out, "out"), T if total_tokens is None else total_tokens,
+                                         ctypes.byref(pool), _dev_ptr(slot_ids, "slot_ids"),
+                                         _stream(stream))
+    _check(rc, "kev_packed_attn_prefill_slots")
     return out
 
 

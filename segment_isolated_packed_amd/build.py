@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkev.so")
 SOURCES = ["kev_api.hip", "kev_schedule.hip", "kev_prefill_bf16.hip", "kev_prefill_f32.hip",
-           "kev_decode.hip"]
+           "kev_decode.hip", "kev_store_kv.hip"]
 ARCH = os.environ.get("KEV_OFFLOAD_ARCH", "gfx950")
 
 

@@ -230,6 +230,45 @@ int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
     return to_status(launch_prefill_f32(pa, head_dim, grid, stream));
 }
 
+int kev_packed_attn_prefill_slots(const void *q, const void *k, const void *v,
+                                  const int32_t *cu_seqlens, int32_t n_seg, int32_t heads,
+                                  int32_t kv_heads, int32_t head_dim, void *out, int32_t total_tokens,
+                                  const kev_kv_pool *pool, const int32_t *slot_ids, void *stream_) {
+    if (!pool || n_seg < 0 || total_tokens < 0 || kv_heads <= 0) return KEV_ERR_INVALID_ARG;
+    if (pool->dtype != KEV_BF16) return KEV_ERR_UNSUPPORTED;
+    if (pool->kv_heads != kv_heads || pool->head_dim != head_dim || pool->n_slots <= 0 ||
+        pool->capacity <= 0)
+        return KEV_ERR_INVALID_ARG;
+    if (n_seg > 0 && (!slot_ids || !pool->data)) return KEV_ERR_INVALID_ARG;
+    if (n_seg > pool->n_slots) return KEV_ERR_BAD_SLOT;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    if (check_enabled() && n_seg > 0) {
+        std::vector<int32_t> ids(n_seg), cu(n_seg + 1);
+        if (hipMemcpyAsync(ids.data(), slot_ids, sizeof(int32_t) * n_seg, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipMemcpyAsync(cu.data(), cu_seqlens, sizeof(int32_t) * (n_seg + 1), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess)
+            return KEV_ERR_DEVICE;
+        std::vector<char> seen(pool->n_slots, 0);
+        for (int32_t s = 0; s < n_seg; ++s) {
+            if (ids[s] < 0 || ids[s] >= pool->n_slots || seen[ids[s]]) return KEV_ERR_BAD_SLOT;
+            seen[ids[s]] = 1;
+            if (cu[s + 1] - cu[s] > pool->capacity) return KEV_ERR_SLOT_OVERFLOW;
+        }
+    }
+    int rc = kev_packed_attn_prefill(q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out,
+                                     total_tokens, KEV_BF16, stream_);
+    if (rc) return rc;
+    if (total_tokens == 0) return KEV_OK;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
+    int32_t *err = nullptr;
+    rc = error_word(dev, &err);
+    if (rc) return rc;
+    StoreKvArgs sa{k, v, cu_seqlens, slot_ids, pool->data, n_seg, total_tokens, kv_heads,
+                   pool->n_slots, pool->capacity, err};
+    return to_status(launch_store_kv(sa, head_dim, stream));
+}
+
 int kev_slot_attn_decode(const void *q, const kev_kv_pool *pool, const int32_t *slot_ids,
                          const int32_t *cache_lens, void *out, const void *k_new,
                          const void *v_new, int32_t n_req, int32_t heads, void *stream_) {

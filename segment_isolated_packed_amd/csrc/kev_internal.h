@@ -115,6 +115,15 @@ struct DecodeArgs {
     int32_t *err;
 };
 
+struct StoreKvArgs {
+    const void *k, *v;        // [total_tokens, kv_heads, head_dim]
+    const int32_t *cu;        // [n_seg + 1]
+    const int32_t *slot_ids;  // [n_seg]
+    void *pool;               // [n_slots][2][kv_heads][capacity][head_dim]
+    int32_t n_seg, total_tokens, kv_heads, n_slots, capacity;
+    int32_t *err;
+};
+
 // Launchers (each lives in the translation unit of its kernel).
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int64_t grid,
@@ -122,5 +131,6 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int64_t g
 hipError_t launch_prefill_f32(const PrefillArgs &a, int32_t head_dim, int64_t grid,
                               hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, int32_t head_dim, hipStream_t s);
+hipError_t launch_store_kv(const StoreKvArgs &a, int32_t head_dim, hipStream_t s);
 
 }  // namespace kev

@@ -313,4 +313,38 @@ def pin_work_counters(orc: oracle.Oracle):
     assert c.effective_flops() == int(2 * 2 * 4 * 2 * allowed.sum())
 
 
+def pin_prefill_to_slot_handoff(orc: oracle.Oracle):
+    """Kev part 2 section 2.2 / primer section 2.2: after a packed prefill stores each question's
+    K/V as rows 0..len-1 of its slot, decoding one more token over that slot equals the last
+    row of a prefill over the question extended by that token; no other pool byte changes."""
+    lens = [5, 0, 1, 9, 3]
+    c = W.make_prefill(lens, 8, 2, 16, W.BF16, seed=21)
+    rng = np.random.default_rng(22)
+    n_slots, cap = 8, 12
+    slots = rng.permutation(n_slots)[:len(lens)].astype(np.int32)
+    pool = _bf16(rng.standard_normal((n_slots, 2, 2, cap, 16)))
+    after = orc.store_kv(c.k, c.v, c.cu_seqlens, slots, pool, W.BF16)
+    cu = c.cu_seqlens
+    changed = set(map(tuple, np.argwhere((after != pool).any(-1)).tolist()))
+    expect = set()
+    for s_, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        for kv, src in ((0, c.k), (1, c.v)):
+            assert np.array_equal(after[slots[s_], kv, :, :b - a], src[a:b].transpose(1, 0, 2))
+            expect |= {(int(slots[s_]), kv, g, i) for g in range(2) for i in range(b - a)}
+    assert changed <= expect
+    # one decode step per non-empty question against the stored slots
+    keep = [s_ for s_ in range(len(lens)) if lens[s_] > 0]
+    qn = _bf16(rng.standard_normal((len(keep), 8, 16)))
+    kn = _bf16(rng.standard_normal((len(keep), 2, 16)))
+    vn = _bf16(rng.standard_normal((len(keep), 2, 16)))
+    out = orc.decode(qn, after, slots[keep], np.array([lens[s_] + 1 for s_ in keep], np.int32), kn, vn, 8, W.BF16)
+    for r, s_ in enumerate(keep):
+        a, b = int(cu[s_]), int(cu[s_ + 1])
+        qx = np.concatenate([c.q[a:b], qn[r][None]], 0)
+        kx = np.concatenate([c.k[a:b], kn[r][None]], 0)
+        vx = np.concatenate([c.v[a:b], vn[r][None]], 0)
+        full = orc.prefill(qx, kx, vx, [0, b - a + 1], 8, 2, 16, W.BF16)
+        assert np.array_equal(out[r], full[-1])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -54,6 +54,27 @@ def test_prefill_argument_checks(lib):
     assert _prefill(lib, n_seg=0, T=3) == K.KEV_ERR_BAD_SEQLENS
 
 
+def _prefill_slots(lib, n_seg=2, kvh=4, d=128, n_slots=8, cap=64, pkvh=4, pd=128, dtype=0, null_pool=False,
+                   null_ids=False):
+    p = ctypes.c_void_p(16)
+    pool = K.KvPool(16, n_slots, cap, pkvh, pd, dtype)
+    return lib.kev_packed_attn_prefill_slots(p, p, p, p, n_seg, 8, kvh, d, p, 10,
+                                             None if null_pool else ctypes.byref(pool),
+                                             None if null_ids else p, None)
+
+
+def test_prefill_slots_argument_checks(lib):
+    # every case fails on the host before any HIP call
+    assert _prefill_slots(lib, null_pool=True) == K.KEV_ERR_INVALID_ARG
+    assert _prefill_slots(lib, dtype=1) == K.KEV_ERR_UNSUPPORTED          # fp32 pool
+    assert _prefill_slots(lib, pkvh=2) == K.KEV_ERR_INVALID_ARG           # pool kv_heads differ
+    assert _prefill_slots(lib, pd=64) == K.KEV_ERR_INVALID_ARG            # pool head_dim differs
+    assert _prefill_slots(lib, cap=0) == K.KEV_ERR_INVALID_ARG
+    assert _prefill_slots(lib, null_ids=True) == K.KEV_ERR_INVALID_ARG
+    assert _prefill_slots(lib, n_seg=9) == K.KEV_ERR_BAD_SLOT             # more questions than slots
+    assert _prefill_slots(lib, n_seg=-1) == K.KEV_ERR_INVALID_ARG
+
+
 def _decode(lib, n_req=4, heads=32, n_slots=8, cap=64, kvh=8, d=128, dtype=0, null=False):
     pool = K.KvPool(16, n_slots, cap, kvh, d, dtype)
     p = None if null else ctypes.c_void_p(16)

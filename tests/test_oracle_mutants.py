@@ -37,6 +37,11 @@ MUTANTS = {
     "decode_group_modulo": ("int32_t r = (int32_t)(u / heads), h = (int32_t)(u % heads), g = h / G;",
                             "int32_t r = (int32_t)(u / heads), h = (int32_t)(u % heads), g = h % kv_heads;"),
     "exp_sign_flipped": ("w[j] = exp(w[j] - m);", "w[j] = exp(m - w[j]);"),
+    "store_slot_by_question_index": ("size_t kdst = (size_t)slot_ids[s] * slot_elems + (size_t)g * plane +",
+                                     "size_t kdst = (size_t)(s % n_slots) * slot_elems + (size_t)g * plane +"),
+    "store_row_off_by_one": ("(size_t)(i - cu[s]) * d;", "(size_t)(i - cu[s] + 1) * d;"),
+    "store_k_from_v": ("memcpy((char *)pool_after + kdst * esz, (const char *)k + src * esz, esz * d);",
+                       "memcpy((char *)pool_after + kdst * esz, (const char *)v + src * esz, esz * d);"),
     "append_k_into_v_plane": (
         "memcpy((char *)pool_after + kdst * esz, (const char *)k_new + src * esz, esz * d);",
         "memcpy((char *)pool_after + vdst * esz, (const char *)k_new + src * esz, esz * d);"),
