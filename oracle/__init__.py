@@ -5,7 +5,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 its binding, and the HIP path never imports it.
 
 ``kev_oracle.c`` holds the plain fp64 loops (full prefill, sampled prefill
-rows, slot-pool decode) and the prefill-to-slot K/V store; ``dense.py`` holds the explicit dense-mask brute
+rows, slot-pool decode), the prefill-to-slot K/V store and chunked prefill
+against a slot prefix; ``dense.py`` holds the explicit dense-mask brute
 force for tiny inputs.  Each function cites the passage of the pages it
 follows in its own header comment or docstring.
 """
@@ -74,9 +75,10 @@ class Oracle:
         L.kev_oracle_prefill_rows.argtypes = [P, P, P, C, P, I, I, I, I, P, P, I, P, C]
         L.kev_oracle_decode.argtypes = [P, P, I, I, I, I, P, P, P, P, I, I, C, P, P, C]
         L.kev_oracle_store_kv.argtypes = [P, P, C, P, I, I, I, P, P, I, I, P]
+        L.kev_oracle_chunked_prefill.argtypes = [P, P, P, C, P, I, I, I, I, P, P, P, I, I, P, P, C]
         L.kev_oracle_max_threads.argtypes = []
         for f in (L.kev_oracle_prefill, L.kev_oracle_prefill_rows, L.kev_oracle_decode,
-                  L.kev_oracle_store_kv, L.kev_oracle_max_threads):
+                  L.kev_oracle_store_kv, L.kev_oracle_chunked_prefill, L.kev_oracle_max_threads):
             f.restype = C
         self._L = L
         self.path = path
@@ -153,6 +155,28 @@ class Oracle:
                                                 kv_heads, d, _ptr(slot_ids), _ptr(pool), n_slots,
                                                 capacity, _ptr(after)))
         return after
+
+    def chunked_prefill(self, q, k, v, cu_seqlens, heads: int, slot_ids, prefix_lens, pool,
+                        dtype: str, n_threads: int = 0):
+        """Chunks continuing cached slot prefixes: returns (out[T, heads, d] fp64, pool after the
+        chunk's K/V rows are appended at rows prefix..prefix+len-1 of each slot)."""
+        q, k, v, pool = (_input(x, dtype) for x in (q, k, v, pool))
+        n_slots, two, kv_heads, capacity, d = pool.shape
+        if two != 2:
+            raise ValueError("pool must be [n_slots, 2, kv_heads, capacity, d]")
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        slot_ids = np.ascontiguousarray(slot_ids, dtype=np.int32)
+        prefix_lens = np.ascontiguousarray(prefix_lens, dtype=np.int32)
+        T = int(cu[-1]) if len(cu) else 0
+        if len(slot_ids) != len(cu) - 1 or len(prefix_lens) != len(cu) - 1 or k.shape[0] != T:
+            raise OracleError(-1)
+        out = np.zeros((T, heads, d), dtype=np.float64)
+        after = np.empty_like(pool)
+        self._check(self._L.kev_oracle_chunked_prefill(
+            _ptr(q), _ptr(k), _ptr(v), _code(dtype), _ptr(cu), len(cu) - 1, heads, kv_heads, d,
+            _ptr(slot_ids), _ptr(prefix_lens), _ptr(pool), n_slots, capacity, _ptr(out), _ptr(after),
+            n_threads))
+        return out, after
 
     def decode_case(self, case, want_pool: bool = False, n_threads: int = 0):
         return self.decode(case.q, case.pool, case.slot_ids, case.cache_lens, case.k_new,

@@ -434,3 +434,103 @@ int kev_oracle_store_kv(const void *k, const void *v, int dtype, const int32_t *
             }
     return ORACLE_OK;
 }
+
+/*
+ * Chunked prefill against a slot prefix: question s's new tokens [cu[s], cu[s+1])
+ * continue the P = prefix_lens[s] rows already cached in slot slot_ids[s].  Query
+ * row i of the chunk sits at position P + i of the question and attends to the
+ * slot's rows 0..P-1 and the chunk's rows 0..i, i.e. the causal mask over the
+ * concatenation (primer, sakurs2.com, sections 2.1 and 2.6: a new chunk's queries
+ * see the cached prefix and their own causal block; Kev part 2, gsyq.cn, section
+ * 2.2: the prefix lives in the question's slot).  The chunk's K/V rows are then
+ * written in place as rows P..P+n-1 of the slot (pool_after; every other byte kept).
+ *   q[T, heads, d], k/v[T, kv_heads, d], pool[n_slots][2][kv_heads][capacity][d];
+ *   out[T, heads, d] double.
+ */
+int kev_oracle_chunked_prefill(const void *q, const void *k, const void *v, int dtype,
+                               const int32_t *cu, int32_t n_seg, int32_t heads, int32_t kv_heads,
+                               int32_t d, const int32_t *slot_ids, const int32_t *prefix_lens,
+                               const void *pool, int32_t n_slots, int32_t capacity, double *out,
+                               void *pool_after, int n_threads)
+{
+    int rc = check_seqlens(cu, n_seg);
+    if (rc)
+        return rc;
+    rc = check_heads(heads, kv_heads, d, dtype);
+    if (rc)
+        return rc;
+    if (n_slots <= 0 || capacity <= 0)
+        return ORACLE_BAD_ARG;
+    for (int32_t s = 0; s < n_seg; s++) {
+        if (slot_ids[s] < 0 || slot_ids[s] >= n_slots)
+            return ORACLE_BAD_SLOT;
+        if (prefix_lens[s] < 0 || prefix_lens[s] + (cu[s + 1] - cu[s]) > capacity)
+            return ORACLE_SLOT_OVERFLOW;
+        for (int32_t s2 = 0; s2 < s; s2++)
+            if (slot_ids[s2] == slot_ids[s])
+                return ORACLE_BAD_SLOT;
+    }
+    size_t esz = dtype == ORACLE_F32 ? 4 : 2;
+    size_t plane = (size_t)capacity * d;
+    size_t slot_elems = (size_t)2 * kv_heads * plane;
+    int G = heads / kv_heads;
+    long units = (long)n_seg * heads;
+    int fail = 0;
+    put_threads(n_threads);
+#pragma omp parallel
+    {
+        double *kbuf = malloc(sizeof(double) * plane);
+        double *vbuf = malloc(sizeof(double) * plane);
+        double *qv = malloc(sizeof(double) * d);
+        double *w = malloc(sizeof(double) * capacity);
+        if (!kbuf || !vbuf || !qv || !w) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic)
+            for (long u = 0; u < units; u++) {
+                int32_t s = (int32_t)(u / heads), h = (int32_t)(u % heads), g = h / G;
+                int32_t a = cu[s], n = cu[s + 1] - cu[s], P = prefix_lens[s];
+                size_t kbase = (size_t)slot_ids[s] * slot_elems + (size_t)g * plane;
+                size_t vbase = (size_t)slot_ids[s] * slot_elems + (size_t)(kv_heads + g) * plane;
+                /* keys 0..P-1 from the slot, P..P+n-1 from the chunk */
+                for (size_t e = 0; e < (size_t)P * d; e++) {
+                    kbuf[e] = widen(pool, dtype, kbase + e);
+                    vbuf[e] = widen(pool, dtype, vbase + e);
+                }
+                for (int32_t j = 0; j < n; j++)
+                    for (int32_t c = 0; c < d; c++) {
+                        size_t src = ((size_t)(a + j) * kv_heads + g) * d + c;
+                        kbuf[(size_t)(P + j) * d + c] = widen(k, dtype, src);
+                        vbuf[(size_t)(P + j) * d + c] = widen(v, dtype, src);
+                    }
+                for (int32_t i = 0; i < n; i++) {
+                    for (int32_t c = 0; c < d; c++)
+                        qv[c] = widen(q, dtype, ((size_t)(a + i) * heads + h) * d + c);
+                    attend(qv, kbuf, vbuf, P + i + 1, d, w, out + ((size_t)(a + i) * heads + h) * d);
+                }
+            }
+        }
+        free(kbuf);
+        free(vbuf);
+        free(qv);
+        free(w);
+    }
+    if (fail)
+        return ORACLE_NO_MEMORY;
+    if (pool_after) {
+        memcpy(pool_after, pool, esz * slot_elems * (size_t)n_slots);
+        for (int32_t s = 0; s < n_seg; s++)
+            for (int32_t i = cu[s]; i < cu[s + 1]; i++)
+                for (int32_t g = 0; g < kv_heads; g++) {
+                    /* element offsets of the K row and the V row P + (i - cu[s]) of head g */
+                    size_t row = (size_t)(prefix_lens[s] + i - cu[s]);
+                    size_t to_k = ((size_t)slot_ids[s] * 2 * kv_heads + g) * plane + row * d;
+                    size_t to_v = ((size_t)slot_ids[s] * 2 * kv_heads + kv_heads + g) * plane + row * d;
+                    size_t from = ((size_t)i * kv_heads + g) * d;
+                    memcpy((char *)pool_after + to_k * esz, (const char *)k + from * esz, esz * d);
+                    memcpy((char *)pool_after + to_v * esz, (const char *)v + from * esz, esz * d);
+                }
+    }
+    return ORACLE_OK;
+}

@@ -347,4 +347,61 @@ def pin_prefill_to_slot_handoff(orc: oracle.Oracle):
         assert np.array_equal(out[r], full[-1])
 
 
+def pin_chunked_prefill_against_slot_prefix(orc: oracle.Oracle):
+    """Primer sections 2.1/2.6 and Kev part 2 section 2.2: a chunk continuing a question whose
+    first P rows sit in its slot attends to those rows and to its own causal block, and its K/V
+    become rows P.. of the slot.  Checked three ways: a dense masked softmax over the explicit
+    key sequence [slot rows 0..P-1 ; chunk rows], P = 0 reducing to the plain prefill and the
+    store, and a question split into two chunks reproducing the unsplit prefill and store."""
+    rng = np.random.default_rng(61)
+    # (1) dense brute force with arbitrary slot contents, fp32
+    lens, pre, hq, hk, d, n_slots, cap = [4, 0, 1, 6], [3, 5, 0, 2], 4, 2, 8, 6, 9
+    c = W.make_prefill(lens, hq, hk, d, W.F32, seed=62)
+    slots = np.array([4, 0, 5, 2], np.int32)
+    pool = _f32(rng.standard_normal((n_slots, 2, hk, cap, d)))
+    out, after = orc.chunked_prefill(c.q, c.k, c.v, c.cu_seqlens, hq, slots, pre, pool, W.F32)
+    q, k, v, pw = (oracle.widen(x, W.F32) for x in (c.q, c.k, c.v, pool))
+    cu = c.cu_seqlens
+    for s_ in range(len(lens)):
+        a, b, P = int(cu[s_]), int(cu[s_ + 1]), pre[s_]
+        for h in range(hq):
+            g = h // (hq // hk)
+            keys = np.concatenate([pw[slots[s_], 0, g, :P], k[a:b, g]], 0)
+            vals = np.concatenate([pw[slots[s_], 1, g, :P], v[a:b, g]], 0)
+            sc = q[a:b, h] @ keys.T / math.sqrt(d)
+            sc[np.arange(P + b - a)[None, :] > P + np.arange(b - a)[:, None]] = -np.inf
+            p_ = np.exp(sc - sc.max(1, keepdims=True))
+            ref = (p_ / p_.sum(1, keepdims=True)) @ vals
+            assert np.abs(out[a:b, h] - ref).max(initial=0) <= 1e-12
+        for kv, src in ((0, c.k), (1, c.v)):
+            assert np.array_equal(after[slots[s_], kv, :, P:P + b - a], src[a:b].transpose(1, 0, 2))
+    untouched = np.ones(after.shape[:4], bool)
+    for s_ in range(len(lens)):
+        untouched[slots[s_], :, :, pre[s_]:pre[s_] + lens[s_]] = False
+    assert np.array_equal(after[untouched], pool[untouched])
+    # (2) empty prefixes: the plain prefill and the prefill-to-slot store, bit for bit
+    c = W.make_prefill([5, 0, 3, 7], 8, 2, 16, W.BF16, seed=63)
+    slots = np.array([1, 3, 0, 2], np.int32)
+    pool = _bf16(rng.standard_normal((4, 2, 2, 8, 16)))
+    out, after = orc.chunked_prefill(c.q, c.k, c.v, c.cu_seqlens, 8, slots, [0] * 4, pool, W.BF16)
+    assert np.array_equal(out, orc.prefill_case(c))
+    assert np.array_equal(after, orc.store_kv(c.k, c.v, c.cu_seqlens, slots, pool, W.BF16))
+    # (3) every question split into two chunks equals the unsplit prefill and store
+    lens, cut = [9, 1, 6, 4], [4, 0, 6, 1]
+    c = W.make_prefill(lens, 8, 2, 16, W.BF16, seed=64)
+    slots = np.array([2, 0, 3, 1], np.int32)
+    pool = _bf16(rng.standard_normal((4, 2, 2, 10, 16)))
+    full, full_pool = orc.prefill_case(c), orc.store_kv(c.k, c.v, c.cu_seqlens, slots, pool, W.BF16)
+    pieces = []
+    for lo, hi in ((np.zeros(4, int), np.array(cut)), (np.array(cut), np.array(lens))):
+        rows = np.concatenate([np.arange(c.cu_seqlens[s_] + lo[s_], c.cu_seqlens[s_] + hi[s_])
+                               for s_ in range(4)]).astype(int)
+        cu2 = np.concatenate([[0], np.cumsum(hi - lo)]).astype(np.int32)
+        o, pool = orc.chunked_prefill(c.q[rows], c.k[rows], c.v[rows], cu2, 8, slots, lo, pool, W.BF16)
+        pieces.append((rows, o))
+    for rows, o in pieces:
+        assert np.array_equal(o, full[rows])
+    assert np.array_equal(pool, full_pool)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -42,6 +42,12 @@ MUTANTS = {
     "store_row_off_by_one": ("(size_t)(i - cu[s]) * d;", "(size_t)(i - cu[s] + 1) * d;"),
     "store_k_from_v": ("memcpy((char *)pool_after + kdst * esz, (const char *)k + src * esz, esz * d);",
                        "memcpy((char *)pool_after + kdst * esz, (const char *)v + src * esz, esz * d);"),
+    "chunk_causal_limit_off_by_one": ("attend(qv, kbuf, vbuf, P + i + 1,", "attend(qv, kbuf, vbuf, P + i,"),
+    "chunk_prefix_keys_from_v_plane": (
+        "kbuf[e] = widen(pool, dtype, kbase + e);", "kbuf[e] = widen(pool, dtype, vbase + e);"),
+    "chunk_rows_overwrite_prefix": ("kbuf[(size_t)(P + j) * d + c] = widen(k, dtype, src);",
+                                    "kbuf[(size_t)j * d + c] = widen(k, dtype, src);"),
+    "chunk_stored_at_row_zero": ("size_t row = (size_t)(prefix_lens[s] + i - cu[s]);", "size_t row = (size_t)(i - cu[s]);"),
     "append_k_into_v_plane": (
         "memcpy((char *)pool_after + kdst * esz, (const char *)k_new + src * esz, esz * d);",
         "memcpy((char *)pool_after + vdst * esz, (const char *)k_new + src * esz, esz * d);"),
