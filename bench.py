@@ -9,7 +9,9 @@ read so the decode reads its KV rows from HBM rather than from the 256 MB MALL.
 Prints ONE JSON line.  `value` is the prefill's effective TFLOP/s (only unmasked score
 entries counted: 4 * d * heads * sum L(L+1)/2 FLOPs per call) over the average duration
 of the prefill call measured with HIP events on the launch stream.  The decode's
-achieved HBM GB/s (algorithmic bytes over event-timed duration) is reported beside it.
+achieved HBM GB/s (algorithmic bytes over event-timed duration) is reported beside it,
+and so are two more calls timed the same way: the prefill that also stores every question's
+K/V into its slot, and a chunked prefill of 8 long prompts against their cached prefixes.
 """
 from __future__ import annotations
 
@@ -90,7 +92,7 @@ def main():
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
                     help="how the 256 MB MALL is evicted before each decode: read a 512 MiB "
                          "buffer (default), write it, or not at all")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "chunked", "copy"], default=None,
                     help="run one half of the step, or a 1 GiB device copy that calibrates "
                          "the HBM byte counters (profiling runs)")
     args = ap.parse_args()
@@ -199,6 +201,35 @@ def main():
         slots_res = {"ms": slots_ms, "store_bytes": store_bytes, "slot_capacity": cap}
         del spool
 
+    # Chunked prefill against slot prefixes (kev_chunked_prefill_slots) on its own workload:
+    # 8 long prompts at four different chunk phases, packed into one call.
+    chunk_res = None
+    if args.only in (None, "chunked"):
+        log("generating chunked-prefill inputs")
+        cc = W.chunked_case()
+        cq, ck, cv, cpool = (to_dev(x, W.BF16) for x in (cc.q, cc.k, cc.v, cc.pool))
+        ccu, cids, cpre = (torch.from_numpy(x).to(dev) for x in (cc.cu_seqlens, cc.slot_ids, cc.prefix_lens))
+        cout = torch.empty_like(cq)
+        for _ in range(max(args.warmup, 1)):
+            K.kev_chunked_prefill_slots(cq, ck, cv, ccu, cpool, cids, cpre, out=cout)
+        torch.cuda.synchronize()
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in cev:
+            e[0].record(stream)
+            K.kev_chunked_prefill_slots(cq, ck, cv, ccu, cpool, cids, cpre, out=cout)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        if K.kev_get_device_errors():
+            raise RuntimeError("device error flags in the chunked-prefill leg")
+        c_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in cev]))
+        c_tf = cc.effective_flops() / (c_ms * 1e-3) / 1e12
+        chunk_res = {
+            "ms": c_ms, "effective_tflops": c_tf, "pct_peak": c_tf / PEAK_BF16_TFLOPS * 100,
+            "effective_gflop": cc.effective_flops() / 1e9, "algorithmic_mb": cc.algorithmic_bytes() / 1e6,
+            "workload": W.CHUNKED_DESCRIPTION, "seed": cc.seed,
+            "call": "kev_chunked_prefill_slots: scheduler + prefill_bf16_kernel<128, prefix> + K/V append"}
+        del cq, ck, cv, cpool, cout
+
     pre_ms = [e[0].elapsed_time(e[1]) for e in events] if do_pre else [float("nan")]
     dec_ms = [e[2].elapsed_time(e[3]) for e in events] if do_dec else [float("nan")]
     pre_avg = float(np.mean(pre_ms))
@@ -256,6 +287,7 @@ def main():
             "store_bytes": slots_res["store_bytes"], "slot_capacity": slots_res["slot_capacity"],
             "store_gbps_incl_launch": slots_res["store_bytes"] / max(slots_res["ms"] - pre_avg, 1e-6) / 1e6,
             "call": "kev_packed_attn_prefill_slots: prefill + every question's K/V stored into its slot"},
+        "chunked_prefill": chunk_res,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and do_pre:

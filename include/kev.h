@@ -1,7 +1,7 @@
 /*
  * kev.h -- C ABI of the segment-isolated packed attention library (gfx950).
  *
- * Two entry points:
+ * Entry points:
  *
  *   kev_packed_attn_prefill  packed prefill.  Several independent questions
  *       are concatenated into one token stream and each token attends only to
@@ -24,6 +24,11 @@
  *   kev_packed_attn_prefill_slots  the prefill, and each question's K/V rows
  *       stored into its slot of that pool (the handoff to decode).
  *
+ *   kev_chunked_prefill_slots  chunked prefill: each question of the packed
+ *       stream is the next chunk of a prompt whose earlier rows are already
+ *       cached in its slot; the chunk attends to them and to itself causally,
+ *       and its K/V rows are appended to the slot.
+ *
  * Conventions shared by every call
  *   - Tensor pointers are DEVICE pointers owned by the caller, contiguous in
  *     the layouts stated below, never freed or retained by the library.
@@ -32,7 +37,7 @@
  *   - Arguments that can be checked without reading device memory are checked
  *     before any HIP call; a failing check returns a negative kev_status and
  *     enqueues nothing.  n_seg == 0 or n_req == 0 is a successful no-op.
- *   - Device-array contents (cu_seqlens, slot_ids, cache_lens) are guarded in
+ *   - Device-array contents (cu_seqlens, slot_ids, cache_lens, prefix_lens) are guarded in
  *     the kernels: an invalid unit is skipped (its outputs are left untouched,
  *     nothing out of range is read or written) and a bit is set in the
  *     per-device error word read by kev_get_device_errors.  With the
@@ -159,6 +164,40 @@ int kev_packed_attn_prefill_slots(const void *q, const void *k, const void *v,
                                   const int32_t *cu_seqlens, int32_t n_seg, int32_t heads,
                                   int32_t kv_heads, int32_t head_dim, void *out, int32_t total_tokens,
                                   const kev_kv_pool *kv_pool, const int32_t *slot_ids, void *stream);
+
+/*
+ * Chunked prefill against a slot prefix.  Question s of the packed stream is
+ * a chunk of len_s = cu_seqlens[s+1] - cu_seqlens[s] tokens that continues the
+ * P_s = prefix_lens[s] rows already held in slot slot_ids[s].  Chunk row i is
+ * position P_s + i of its question and attends, under the causal mask of the
+ * primer (sakurs2.com, sections 2.1 and 2.6), to slot rows 0..P_s-1 and chunk
+ * rows 0..i of its own question only; other questions stay invisible (Kev
+ * article, icman.com.cn, sections 2.1 and 2.3).  The slot is the question's
+ * own (Kev part 2, gsyq.cn, section 2.2).  After the call the chunk's K and V
+ * rows are rows P_s..P_s+len_s-1 of the slot (every KV head), written in place.
+ *
+ *   q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out, total_tokens:
+ *                as for kev_packed_attn_prefill (bf16 only), describing the
+ *                chunks' own tokens
+ *   kv_pool      host pointer to the pool descriptor; kv_heads and head_dim
+ *                must equal the call's, dtype KEV_BF16
+ *   slot_ids     int32 [n_seg], device; distinct slots in [0, n_slots)
+ *   prefix_lens  int32 [n_seg], device; cached rows per question, with
+ *                0 <= P_s and P_s + len_s <= capacity (P_s = 0 is a fresh
+ *                question: the call then equals kev_packed_attn_prefill_slots)
+ *
+ * The prefix rows are read, never written; rows past P_s + len_s and other
+ * slots are untouched.  A question whose slot id is out of range, or whose
+ * rows overflow the slot, gets neither output rows nor stored rows
+ * (KEV_DEVERR_SLOT / KEV_DEVERR_CACHE_LEN in the device error word;
+ * KEV_ERR_BAD_SLOT / KEV_ERR_SLOT_OVERFLOW under KEV_CHECK=1, which also
+ * rejects repeated slot ids).
+ */
+int kev_chunked_prefill_slots(const void *q, const void *k, const void *v,
+                              const int32_t *cu_seqlens, int32_t n_seg, int32_t heads,
+                              int32_t kv_heads, int32_t head_dim, void *out, int32_t total_tokens,
+                              const kev_kv_pool *kv_pool, const int32_t *slot_ids,
+                              const int32_t *prefix_lens, void *stream);
 
 /* Human-readable text for a kev_status value (static storage). */
 const char *kev_status_string(int status);

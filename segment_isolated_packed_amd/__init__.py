@@ -60,6 +60,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kev_packed_attn_prefill.argtypes = [P, P, P, P, I, I, I, I, P, I, I, P]
     L.kev_slot_attn_decode.argtypes = [P, ctypes.POINTER(KvPool), P, P, P, P, P, I, I, P]
     L.kev_packed_attn_prefill_slots.argtypes = [P, P, P, P, I, I, I, I, P, I, ctypes.POINTER(KvPool), P, P]
+    L.kev_chunked_prefill_slots.argtypes = [P, P, P, P, I, I, I, I, P, I, ctypes.POINTER(KvPool), P, P, P]
     L.kev_status_string.argtypes = [ctypes.c_int]
     L.kev_status_string.restype = ctypes.c_char_p
     L.kev_get_device_errors.argtypes = [P, ctypes.POINTER(I)]
@@ -68,7 +69,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kev_schedule_host.argtypes = [P, I, I, I, P, I, ctypes.POINTER(I)]
     L.kev_schedule_device.argtypes = [P, I, I, I, I, P, I, ctypes.POINTER(I), P]
     for f in (L.kev_packed_attn_prefill, L.kev_slot_attn_decode, L.kev_packed_attn_prefill_slots,
-              L.kev_get_device_errors,
+              L.kev_chunked_prefill_slots, L.kev_get_device_errors,
               L.kev_prefill_block_rows, L.kev_prefill_order, L.kev_schedule_host,
               L.kev_schedule_device):
         f.restype = ctypes.c_int
@@ -171,14 +172,7 @@ def kev_slot_attn_decode(q, kv_pool, slot_ids, cache_lens, k_new, v_new, out=Non
     return out
 
 
-def kev_packed_attn_prefill_slots(q, k, v, cu_seqlens, kv_pool, slot_ids, out=None,
-                                  total_tokens: int | None = None, stream=None):
-    """Packed prefill that also stores question s's K/V rows as rows 0..len-1 of slot
-    slot_ids[s] of kv_pool (bf16, [n_slots, 2, kv_heads, capacity, d], updated in place).
-
-    q [T, heads, d], k/v [T, kv_heads, d] (bf16), cu_seqlens / slot_ids int32 on the device.
-    Returns out [T, heads, d].
-    """
+def _slot_prefill(name, q, k, v, cu_seqlens, kv_pool, slot_ids, prefix_lens, out, total_tokens, stream):
     import torch
     L = load_library()
     T, heads, d = q.shape
@@ -191,25 +185,54 @@ def kev_packed_attn_prefill_slots(q, k, v, cu_seqlens, kv_pool, slot_ids, out=No
     for t in (k, v, kv_pool):
         if t.dtype != q.dtype:
             raise TypeError("q, k, v, kv_pool must share one dtype")
-    for name, t in (("cu_seqlens", cu_seqlens), ("slot_ids", slot_ids)):
+    ints = [("cu_seqlens", cu_seqlens), ("slot_ids", slot_ids)]
+    if prefix_lens is not None:
+        ints.append(("prefix_lens", prefix_lens))
+    for nm, t in ints:
         if t.dtype != torch.int32:
-            raise TypeError(f"{name} must be int32")
+            raise TypeError(f"{nm} must be int32")
     n_seg = cu_seqlens.numel() - 1
-    if slot_ids.numel() != n_seg:
-        raise ValueError("slot_ids must have one entry per question")
+    for nm, t in ints[1:]:
+        if t.numel() != n_seg:
+            raise ValueError(f"{nm} must have one entry per question")
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q")
     pool = KvPool(_dev_ptr(kv_pool, "kv_pool").value, n_slots, capacity, kv_heads, d,
                   _dtype_code(kv_pool))
-    rc = L.kev_packed_attn_prefill_slots(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                                         _dev_ptr(cu_seqlens, "cu_seqlens"), n_seg, heads, kv_heads,
-                                         d, _dev_ptr(out, "out"), T if total_tokens is None else total_tokens,
-                                         ctypes.byref(pool), _dev_ptr(slot_ids, "slot_ids"),
-                                         _stream(stream))
-    _check(rc, "kev_packed_attn_prefill_slots")
+    args = [_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(cu_seqlens, "cu_seqlens"), n_seg,
+            heads, kv_heads, d, _dev_ptr(out, "out"), T if total_tokens is None else total_tokens,
+            ctypes.byref(pool), _dev_ptr(slot_ids, "slot_ids")]
+    if prefix_lens is not None:
+        args.append(_dev_ptr(prefix_lens, "prefix_lens"))
+    _check(getattr(L, name)(*args, _stream(stream)), name)
     return out
+
+
+def kev_packed_attn_prefill_slots(q, k, v, cu_seqlens, kv_pool, slot_ids, out=None,
+                                  total_tokens: int | None = None, stream=None):
+    """Packed prefill that also stores question s's K/V rows as rows 0..len-1 of slot
+    slot_ids[s] of kv_pool (bf16, [n_slots, 2, kv_heads, capacity, d], updated in place).
+
+    q [T, heads, d], k/v [T, kv_heads, d] (bf16), cu_seqlens / slot_ids int32 on the device.
+    Returns out [T, heads, d].
+    """
+    return _slot_prefill("kev_packed_attn_prefill_slots", q, k, v, cu_seqlens, kv_pool, slot_ids, None,
+                         out, total_tokens, stream)
+
+
+def kev_chunked_prefill_slots(q, k, v, cu_seqlens, kv_pool, slot_ids, prefix_lens, out=None,
+                              total_tokens: int | None = None, stream=None):
+    """Chunked prefill: question s of the packed stream continues the prefix_lens[s] rows
+    cached in slot slot_ids[s] of kv_pool; its rows attend to those and to their own causal
+    block, and its K/V rows are appended to the slot (rows prefix..prefix+len-1, in place).
+
+    q [T, heads, d], k/v [T, kv_heads, d] (bf16); cu_seqlens, slot_ids, prefix_lens int32 on
+    the device.  Returns out [T, heads, d].
+    """
+    return _slot_prefill("kev_chunked_prefill_slots", q, k, v, cu_seqlens, kv_pool, slot_ids, prefix_lens,
+                         out, total_tokens, stream)
 
 
 def kev_get_device_errors(stream=None) -> int:

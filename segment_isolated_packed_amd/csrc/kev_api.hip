@@ -143,34 +143,16 @@ int run_schedule(const int32_t *cu, int32_t n_seg, int32_t total_tokens, int32_t
     return KEV_OK;
 }
 
-}  // namespace
+// Slot side of a chunked prefill: question s continues prefix_lens[s] rows of slot slot_ids[s].
+struct SlotPrefix {
+    const kev_kv_pool *pool;
+    const int32_t *slot_ids, *prefix_lens;
+};
 
-extern "C" {
-
-const char *kev_status_string(int status) {
-    switch (status) {
-    case KEV_OK: return "ok";
-    case KEV_ERR_INVALID_ARG: return "invalid argument";
-    case KEV_ERR_UNSUPPORTED: return "unsupported dtype/head_dim combination";
-    case KEV_ERR_BAD_SEQLENS: return "cu_seqlens must start at 0, be non-decreasing and end at total_tokens";
-    case KEV_ERR_SLOT_OVERFLOW: return "cache length outside [1, slot capacity]";
-    case KEV_ERR_BAD_SLOT: return "slot id out of range or repeated";
-    case KEV_ERR_DEVICE: return "HIP runtime error";
-    case KEV_ERR_NO_MEMORY: return "workspace allocation failed";
-    default: return "unknown status";
-    }
-}
-
-int kev_prefill_block_rows(int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype) {
-    if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0) return 0;
-    if (!prefill_supported(head_dim, dtype)) return 0;
-    return block_rows_for(heads, kv_heads, dtype);
-}
-
-int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
-                            const int32_t *cu_seqlens, int32_t n_seg,
-                            int32_t heads, int32_t kv_heads, int32_t head_dim,
-                            void *out, int32_t total_tokens, int32_t dtype, void *stream_) {
+// Packed prefill; with `pre`, every question is a chunk continuing its slot's cached rows.
+int prefill_impl(const void *q, const void *k, const void *v, const int32_t *cu_seqlens, int32_t n_seg,
+                 int32_t heads, int32_t kv_heads, int32_t head_dim, void *out, int32_t total_tokens,
+                 int32_t dtype, void *stream_, const SlotPrefix *pre) {
     if (n_seg < 0 || total_tokens < 0 || heads <= 0 || kv_heads <= 0 || head_dim <= 0)
         return KEV_ERR_INVALID_ARG;
     if (heads % kv_heads != 0) return KEV_ERR_INVALID_ARG;
@@ -219,8 +201,20 @@ int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
         pa.wg_per_kvh = sh.wg_per_kvh;
         const int64_t grid = n_max * kv_heads * sh.wg_per_kvh;
         if (grid > INT32_MAX) return KEV_ERR_INVALID_ARG;
-        return to_status(launch_prefill_bf16(pa, head_dim, grid, stream));
+        if (pre) {
+            int dev = 0;
+            if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
+            rc = error_word(dev, &pa.err);
+            if (rc) return rc;
+            pa.slot_ids = pre->slot_ids;
+            pa.prefix_lens = pre->prefix_lens;
+            pa.pool = pre->pool->data;
+            pa.n_slots = pre->pool->n_slots;
+            pa.capacity = pre->pool->capacity;
+        }
+        return to_status(launch_prefill_bf16(pa, head_dim, grid, pre != nullptr, stream));
     }
+    if (pre) return KEV_ERR_UNSUPPORTED;
     pa.heads_per_wg = 1;
     pa.row_blocks = 1;
     pa.block_rows = kF32BlockRows;
@@ -230,10 +224,9 @@ int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
     return to_status(launch_prefill_f32(pa, head_dim, grid, stream));
 }
 
-int kev_packed_attn_prefill_slots(const void *q, const void *k, const void *v,
-                                  const int32_t *cu_seqlens, int32_t n_seg, int32_t heads,
-                                  int32_t kv_heads, int32_t head_dim, void *out, int32_t total_tokens,
-                                  const kev_kv_pool *pool, const int32_t *slot_ids, void *stream_) {
+// Arguments shared by the two slot-writing prefills: a bf16 pool that matches the K/V heads.
+int check_pool(const kev_kv_pool *pool, int32_t n_seg, int32_t total_tokens, int32_t kv_heads,
+               int32_t head_dim, const int32_t *slot_ids) {
     if (!pool || n_seg < 0 || total_tokens < 0 || kv_heads <= 0) return KEV_ERR_INVALID_ARG;
     if (pool->dtype != KEV_BF16) return KEV_ERR_UNSUPPORTED;
     if (pool->kv_heads != kv_heads || pool->head_dim != head_dim || pool->n_slots <= 0 ||
@@ -241,32 +234,111 @@ int kev_packed_attn_prefill_slots(const void *q, const void *k, const void *v,
         return KEV_ERR_INVALID_ARG;
     if (n_seg > 0 && (!slot_ids || !pool->data)) return KEV_ERR_INVALID_ARG;
     if (n_seg > pool->n_slots) return KEV_ERR_BAD_SLOT;
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
-    if (check_enabled() && n_seg > 0) {
-        std::vector<int32_t> ids(n_seg), cu(n_seg + 1);
-        if (hipMemcpyAsync(ids.data(), slot_ids, sizeof(int32_t) * n_seg, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-            hipMemcpyAsync(cu.data(), cu_seqlens, sizeof(int32_t) * (n_seg + 1), hipMemcpyDeviceToHost, stream) != hipSuccess ||
-            hipStreamSynchronize(stream) != hipSuccess)
-            return KEV_ERR_DEVICE;
-        std::vector<char> seen(pool->n_slots, 0);
-        for (int32_t s = 0; s < n_seg; ++s) {
-            if (ids[s] < 0 || ids[s] >= pool->n_slots || seen[ids[s]]) return KEV_ERR_BAD_SLOT;
-            seen[ids[s]] = 1;
-            if (cu[s + 1] - cu[s] > pool->capacity) return KEV_ERR_SLOT_OVERFLOW;
-        }
+    return KEV_OK;
+}
+
+// KEV_CHECK: slot ids in range and distinct, and every question's rows (after its prefix,
+// if any) fit the slot.
+int host_check_slots(const kev_kv_pool *pool, const int32_t *slot_ids, const int32_t *prefix_lens,
+                     const int32_t *cu_seqlens, int32_t n_seg, hipStream_t stream) {
+    std::vector<int32_t> ids(n_seg), cu(n_seg + 1), pre(n_seg, 0);
+    if (hipMemcpyAsync(ids.data(), slot_ids, sizeof(int32_t) * n_seg, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipMemcpyAsync(cu.data(), cu_seqlens, sizeof(int32_t) * (n_seg + 1), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        (prefix_lens && hipMemcpyAsync(pre.data(), prefix_lens, sizeof(int32_t) * n_seg, hipMemcpyDeviceToHost,
+                                       stream) != hipSuccess) ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return KEV_ERR_DEVICE;
+    std::vector<char> seen(pool->n_slots, 0);
+    for (int32_t s = 0; s < n_seg; ++s) {
+        if (ids[s] < 0 || ids[s] >= pool->n_slots || seen[ids[s]]) return KEV_ERR_BAD_SLOT;
+        seen[ids[s]] = 1;
+        if (pre[s] < 0 || (int64_t)pre[s] + cu[s + 1] - cu[s] > pool->capacity) return KEV_ERR_SLOT_OVERFLOW;
     }
-    int rc = kev_packed_attn_prefill(q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out,
-                                     total_tokens, KEV_BF16, stream_);
-    if (rc) return rc;
-    if (total_tokens == 0) return KEV_OK;
+    return KEV_OK;
+}
+
+// Write every question's K/V rows into its slot, after its prefix rows if any.
+int store_rows(const void *k, const void *v, const int32_t *cu_seqlens, int32_t n_seg, int32_t kv_heads,
+               int32_t head_dim, int32_t total_tokens, const kev_kv_pool *pool, const int32_t *slot_ids,
+               const int32_t *prefix_lens, hipStream_t stream) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
     int32_t *err = nullptr;
-    rc = error_word(dev, &err);
+    int rc = error_word(dev, &err);
     if (rc) return rc;
-    StoreKvArgs sa{k, v, cu_seqlens, slot_ids, pool->data, n_seg, total_tokens, kv_heads,
+    StoreKvArgs sa{k, v, cu_seqlens, slot_ids, prefix_lens, pool->data, n_seg, total_tokens, kv_heads,
                    pool->n_slots, pool->capacity, err};
     return to_status(launch_store_kv(sa, head_dim, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kev_status_string(int status) {
+    switch (status) {
+    case KEV_OK: return "ok";
+    case KEV_ERR_INVALID_ARG: return "invalid argument";
+    case KEV_ERR_UNSUPPORTED: return "unsupported dtype/head_dim combination";
+    case KEV_ERR_BAD_SEQLENS: return "cu_seqlens must start at 0, be non-decreasing and end at total_tokens";
+    case KEV_ERR_SLOT_OVERFLOW: return "cache length (or prefix plus chunk rows) outside the slot capacity";
+    case KEV_ERR_BAD_SLOT: return "slot id out of range or repeated";
+    case KEV_ERR_DEVICE: return "HIP runtime error";
+    case KEV_ERR_NO_MEMORY: return "workspace allocation failed";
+    default: return "unknown status";
+    }
+}
+
+int kev_prefill_block_rows(int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype) {
+    if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0) return 0;
+    if (!prefill_supported(head_dim, dtype)) return 0;
+    return block_rows_for(heads, kv_heads, dtype);
+}
+
+int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
+                            const int32_t *cu_seqlens, int32_t n_seg,
+                            int32_t heads, int32_t kv_heads, int32_t head_dim,
+                            void *out, int32_t total_tokens, int32_t dtype, void *stream) {
+    return prefill_impl(q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out, total_tokens, dtype,
+                        stream, nullptr);
+}
+
+int kev_packed_attn_prefill_slots(const void *q, const void *k, const void *v,
+                                  const int32_t *cu_seqlens, int32_t n_seg, int32_t heads,
+                                  int32_t kv_heads, int32_t head_dim, void *out, int32_t total_tokens,
+                                  const kev_kv_pool *pool, const int32_t *slot_ids, void *stream_) {
+    int rc = check_pool(pool, n_seg, total_tokens, kv_heads, head_dim, slot_ids);
+    if (rc) return rc;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    if (check_enabled() && n_seg > 0) {
+        rc = host_check_slots(pool, slot_ids, nullptr, cu_seqlens, n_seg, stream);
+        if (rc) return rc;
+    }
+    rc = prefill_impl(q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out, total_tokens, KEV_BF16,
+                      stream_, nullptr);
+    if (rc || total_tokens == 0) return rc;
+    return store_rows(k, v, cu_seqlens, n_seg, kv_heads, head_dim, total_tokens, pool, slot_ids, nullptr,
+                      stream);
+}
+
+int kev_chunked_prefill_slots(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
+                              int32_t n_seg, int32_t heads, int32_t kv_heads, int32_t head_dim, void *out,
+                              int32_t total_tokens, const kev_kv_pool *pool, const int32_t *slot_ids,
+                              const int32_t *prefix_lens, void *stream_) {
+    int rc = check_pool(pool, n_seg, total_tokens, kv_heads, head_dim, slot_ids);
+    if (rc) return rc;
+    if (n_seg > 0 && !prefix_lens) return KEV_ERR_INVALID_ARG;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    if (check_enabled() && n_seg > 0) {
+        rc = host_check_slots(pool, slot_ids, prefix_lens, cu_seqlens, n_seg, stream);
+        if (rc) return rc;
+    }
+    const SlotPrefix pre{pool, slot_ids, prefix_lens};
+    rc = prefill_impl(q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out, total_tokens, KEV_BF16,
+                      stream_, &pre);
+    if (rc || total_tokens == 0) return rc;
+    return store_rows(k, v, cu_seqlens, n_seg, kv_heads, head_dim, total_tokens, pool, slot_ids, prefix_lens,
+                      stream);
 }
 
 int kev_slot_attn_decode(const void *q, const kev_kv_pool *pool, const int32_t *slot_ids,

@@ -72,7 +72,7 @@ constexpr int32_t kOrderLevel = 1;
 // Workspace layout of the scheduler (int32 units):
 //   [0] n_items  [1..3] unused  [4..] hist[hist_len] | fill[hist_len] | cnt[hist_len] |
 //   start[hist_len] | sigma[n_seg] | qoff[n_seg] | items[2 * max_items] (question, t) |
-//   rec[4 * max_items] ({question start, question length, t, 0}, 16-byte aligned)
+//   rec[4 * max_items] ({question start, question length, t, question index}, 16-byte aligned)
 struct ScheduleLayout {
     int64_t hist, fill, cnt, start, sigma, qoff, items, rec, total;
 };
@@ -96,11 +96,17 @@ struct PrefillArgs {
     const int32_t *cu;
     const int32_t *sched;     // scheduler workspace (n_items at [0], items at items_off)
     int64_t items_off;
-    const int32_t *rec;       // item records {question start, length, t, 0}
+    const int32_t *rec;       // item records {question start, length, t, question index}
     int32_t heads, kv_heads, group;     // group = heads / kv_heads
     int32_t heads_per_wg, row_blocks, block_rows, n_hgroups;   // fp32 path
     int32_t wg_per_kvh;                 // bf16 path: workgroups per item and KV head
     float scale_log2;                   // log2(e) / sqrt(head_dim)
+    // Chunked prefill only: question s continues the prefix_lens[s] rows cached in slot
+    // slot_ids[s] of the pool [n_slots][2][kv_heads][capacity][head_dim].
+    const int32_t *slot_ids, *prefix_lens;
+    const void *pool;
+    int32_t n_slots, capacity;
+    int32_t *err;
 };
 
 struct DecodeArgs {
@@ -119,6 +125,7 @@ struct StoreKvArgs {
     const void *k, *v;        // [total_tokens, kv_heads, head_dim]
     const int32_t *cu;        // [n_seg + 1]
     const int32_t *slot_ids;  // [n_seg]
+    const int32_t *prefix_lens;   // [n_seg] rows already in each slot, or null (all 0)
     void *pool;               // [n_slots][2][kv_heads][capacity][head_dim]
     int32_t n_seg, total_tokens, kv_heads, n_slots, capacity;
     int32_t *err;
@@ -127,7 +134,7 @@ struct StoreKvArgs {
 // Launchers (each lives in the translation unit of its kernel).
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int64_t grid,
-                               hipStream_t s);
+                               bool prefix, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, int32_t head_dim, int64_t grid,
                               hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, int32_t head_dim, hipStream_t s);

@@ -67,13 +67,14 @@ __device__ __forceinline__ void barrier() {
     asm volatile("" ::: "memory");
 }
 
-// 64 lanes x 16 B from global straight into LDS at lds_base + 16*lane
-// (global_load_lds_dwordx4; the LDS base goes through m0).  Issued as inline asm so
-// the compiler does not add its own conservative vmcnt waits before LDS reads: the
-// callers wait for these loads explicitly (wait_vmcnt + barrier) before reading the
-// stage they fill, and never read a stage that has loads in flight.
-__device__ __forceinline__ void dma16(const void *g, const lds_t *lds_base) {
-    const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
+// 64 lanes x 16 B from global straight into LDS at lds_addr + 16*lane
+// (global_load_lds_dwordx4; the LDS address goes through m0), each lane from its own
+// 64-bit address.  Issued as inline asm so the compiler does not add its own
+// conservative vmcnt waits before LDS reads: the callers wait for these loads
+// explicitly (wait_vmcnt + barrier) before reading the stage they fill, and never read
+// a stage that has loads in flight.
+__device__ __forceinline__ void dma16(const void *g, unsigned lds_addr) {
+    const unsigned m0v = __builtin_amdgcn_readfirstlane(lds_addr);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(g), "s"(m0v)

@@ -50,8 +50,20 @@
 // Only tiles inside the item's own question and at or left of its diagonal are
 // loaded; the causal select (-inf, not a multiply) is applied only to tiles
 // that cross a wavefront's diagonal or the end of the question.
+//
+// Chunked prefill (the PREFIX instantiation).  A question of the packed stream
+// may be a chunk that continues P rows already cached in its slot of the KV
+// pool: chunk row i is position P + i of the question and attends to the
+// slot's rows 0..P-1 and the chunk's rows 0..i (primer, sakurs2.com, sections
+// 2.1 and 2.6; the slot is the question's own, Kev part 2, gsyq.cn, section
+// 2.2).  The kernel then walks the concatenated key sequence [slot rows ;
+// chunk rows]: key tiles wholly inside the prefix are loaded from the slot
+// (contiguous rows), tiles wholly inside the chunk from the packed K/V, and the
+// one tile that straddles the boundary per lane from either.  The diagonal and
+// the question end move right by P; everything else is unchanged.
 #include <type_traits>
 
+#include "../../include/kev.h"
 #include "kev_internal.h"
 #include "kev_mfma_core.h"
 
@@ -84,25 +96,33 @@ struct Cfg {
 // address is a wave-uniform tile base plus a per-lane offset that is the same for every
 // full tile.  In the tile that holds key_end, rows at or past key_end are clamped to
 // key_end - 1: a row of the same question, so nothing outside it is read.
-template <int D, int NW>
+//
+// With PREFIX, key index kk < prefix is row kk of the slot's plane (rows D elements apart)
+// and kk >= prefix is row kk - prefix of the packed K/V.
+template <int D, int NW, bool PREFIX>
 struct TileLoader {
     static constexpr int RPI = Geom<D>::RPI;
     static constexpr int IPT = KT / RPI;
     static constexpr int NIT = (IPT + NW - 1) / NW;
+    static constexpr int PROW = D * 2;   // bytes per slot row
     unsigned voff[NIT];     // byte offset of this lane's chunk inside a full tile
     unsigned lds_row[NIT];  // LDS byte offset of the load's first row inside a stage
-    const char *kbase, *vbase;  // tile 0
-    int64_t tile_step;          // bytes between consecutive tiles
+    const char *kbase, *vbase;  // packed K/V row of key `prefix`
+    const char *pkbase, *pvbase;  // slot K/V planes (PREFIX only)
     int row_bytes;
     int key_end;
+    int prefix;
 
     __device__ static int first_row(int wave, int i) { return ((wave + NW * i) % IPT) * RPI; }
 
-    __device__ void init(const uint16_t *k, const uint16_t *v, int64_t row_stride, int kend, int wave) {
+    __device__ void init(const uint16_t *k, const uint16_t *v, int64_t row_stride, int kend, int wave,
+                         const uint16_t *pk = nullptr, const uint16_t *pv = nullptr, int p = 0) {
         kbase = reinterpret_cast<const char *>(k);
         vbase = reinterpret_cast<const char *>(v);
+        pkbase = reinterpret_cast<const char *>(pk);
+        pvbase = reinterpret_cast<const char *>(pv);
+        prefix = PREFIX ? p : 0;
         row_bytes = (int)(row_stride * 2);
-        tile_step = (int64_t)row_bytes * KT;
         key_end = kend;
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
@@ -114,9 +134,34 @@ struct TileLoader {
         }
     }
 
-    __device__ __forceinline__ void issue(const char *base, int tile, unsigned stage_addr, int wave) const {
+    __device__ __forceinline__ void issue(const char *base, const char *pbase, int tile, unsigned stage_addr,
+                                          int wave) const {
         const int k0 = tile * KT;
-        const char *tb = base + (int64_t)tile * tile_step;
+        if constexpr (PREFIX) {
+            if (k0 + KT <= prefix) {   // whole tile in the slot
+                const char *tb = pbase + (int64_t)k0 * PROW;
+#pragma unroll
+                for (int i = 0; i < NIT; ++i) {
+                    DmaLane<D> ln;
+                    ln.init(first_row(wave, i));
+                    dma16s(tb, (unsigned)(ln.row * PROW + ln.coff * 2), stage_addr + lds_row[i]);
+                }
+                return;
+            }
+            if (k0 < prefix) {         // straddles the slot / chunk boundary: per-lane source
+#pragma unroll
+                for (int i = 0; i < NIT; ++i) {
+                    DmaLane<D> ln;
+                    ln.init(first_row(wave, i));
+                    const int kk = min(k0 + ln.row, key_end - 1);
+                    const char *g = kk < prefix ? pbase + (int64_t)kk * PROW + ln.coff * 2
+                                                : base + (int64_t)(kk - prefix) * row_bytes + ln.coff * 2;
+                    dma16(g, stage_addr + lds_row[i]);
+                }
+                return;
+            }
+        }
+        const char *tb = base + (int64_t)(k0 - prefix) * row_bytes;
         if (k0 + KT <= key_end) {
 #pragma unroll
             for (int i = 0; i < NIT; ++i) dma16s(tb, voff[i], stage_addr + lds_row[i]);
@@ -217,7 +262,7 @@ __device__ __forceinline__ void mask_tile(f32x16 &s, int k0, int qrow, int L) {
     }
 }
 
-template <int D>
+template <int D, bool PREFIX>
 __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(PrefillArgs p) {
     using C = Cfg<D>;
@@ -232,7 +277,7 @@ void prefill_bf16_kernel(PrefillArgs p) {
     const int per_item = p.kv_heads * p.wg_per_kvh;
     const int item = blockIdx.x / per_item;
     const __attribute__((address_space(4))) int *recs = (const __attribute__((address_space(4))) int *)p.rec;
-    const int a = recs[4 * item], L = recs[4 * item + 1], t = recs[4 * item + 2];
+    const int a = recs[4 * item], L = recs[4 * item + 1], t = recs[4 * item + 2], sq = recs[4 * item + 3];
     const int32_t n_items = ((const __attribute__((address_space(4))) int *)p.sched)[0];
     if (item >= n_items) return;
     const int rem = blockIdx.x - item * per_item;
@@ -242,7 +287,24 @@ void prefill_bf16_kernel(PrefillArgs p) {
     const int item_row0 = t * p.block_rows;
     const int wg_row_lo = item_row0 + ((NWAVE * w) / G) * 32;
     if (wg_row_lo >= L) return;   // every wavefront of this workgroup is past the question
-    const int wg_key_end = min(item_row0 + ((NWAVE * w + NWAVE - 1) / G + 1) * 32, L);
+
+    // Keys are indexed in the question: P cached rows (chunked prefill), then the L rows here.
+    int P = 0;
+    const uint16_t *pk = nullptr, *pv = nullptr;
+    if constexpr (PREFIX) {
+        const int slot = p.slot_ids[sq];
+        P = p.prefix_lens[sq];
+        const bool bad_slot = slot < 0 || slot >= p.n_slots;
+        if (bad_slot || P < 0 || P > p.capacity - L) {   // the question's rows are not written
+            if (threadIdx.x == 0 && t == 0 && rem == 0)
+                atomicOr(p.err, (int32_t)(bad_slot ? KEV_DEVERR_SLOT : KEV_DEVERR_CACHE_LEN));
+            return;
+        }
+        const int64_t plane = (int64_t)p.capacity * D;
+        pk = static_cast<const uint16_t *>(p.pool) + ((int64_t)slot * 2 * p.kv_heads + kvh) * plane;
+        pv = pk + (int64_t)p.kv_heads * plane;
+    }
+    const int wg_key_end = P + min(item_row0 + ((NWAVE * w + NWAVE - 1) / G + 1) * 32, L);
     const int n_tiles = (wg_key_end + KT - 1) / KT;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -252,9 +314,9 @@ void prefill_bf16_kernel(PrefillArgs p) {
     const int rb = u / G;
     const int head = kvh * G + (u - rb * G);
     const int row0 = item_row0 + rb * 32;                       // question-relative
-    const int wave_key_end = row0 < L ? min(row0 + 32, L) : 0;
+    const int wave_key_end = row0 < L ? P + min(row0 + 32, L) : 0;
     const int my_tiles = (wave_key_end + KT - 1) / KT;
-    const int n_full = min(row0 + 1, L) / KT;                   // tiles needing no mask
+    const int n_full = (P + min(row0 + 1, L)) / KT;             // tiles needing no mask
 
     const int64_t kv_stride = (int64_t)p.kv_heads * D;
     const uint16_t *kg = static_cast<const uint16_t *>(p.k) + ((int64_t)a * p.kv_heads + kvh) * D;
@@ -273,8 +335,8 @@ void prefill_bf16_kernel(PrefillArgs p) {
     st.pending = false;
     const float c = p.scale_log2;
 
-    TileLoader<D, NWAVE> ld;
-    ld.init(kg, vg, kv_stride, wg_key_end, wave);
+    TileLoader<D, NWAVE, PREFIX> ld;
+    ld.init(kg, vg, kv_stride, wg_key_end, wave, pk, pv, P);
     auto kaddr = [&](int s) { return lds0 + (unsigned)(s * C::TB); };
     auto vaddr = [&](int s) { return lds0 + (unsigned)((NS + s) * C::TB); };
 
@@ -294,10 +356,10 @@ void prefill_bf16_kernel(PrefillArgs p) {
     // Issue order: K(0); then, per (virtual) iteration i, K(i+NS) and V(i+NS-1).  At the
     // barrier of iteration j the wave needs K(j+1) and V(j), both issued at iteration
     // j-NS+1 with V last; the loads of at most NS-2 later iterations may stay in flight.
-    ld.issue(ld.kbase, 0, kaddr(0), wave);
+    ld.issue(ld.kbase, ld.pkbase, 0, kaddr(0), wave);
     for (int i = 1 - NS; i < 0; ++i) {
-        if (i + NS < n_tiles) ld.issue(ld.kbase, i + NS, kaddr(i + NS), wave);
-        if (i + NS - 1 < n_tiles) ld.issue(ld.vbase, i + NS - 1, vaddr(i + NS - 1), wave);
+        if (i + NS < n_tiles) ld.issue(ld.kbase, ld.pkbase, i + NS, kaddr(i + NS), wave);
+        if (i + NS - 1 < n_tiles) ld.issue(ld.vbase, ld.pvbase, i + NS - 1, vaddr(i + NS - 1), wave);
     }
     if (n_tiles >= NS) wait_vmcnt<2 * C::NIT * (NS - 1)>();   // q and K(0) have landed
     else wait_vmcnt<0>();
@@ -333,8 +395,8 @@ void prefill_bf16_kernel(PrefillArgs p) {
         if (j + NS - 1 < n_tiles) wait_vmcnt<2 * C::NIT * (NS - 2)>();
         else wait_vmcnt<0>();
         barrier();
-        if (j + NS < n_tiles) ld.issue(ld.kbase, j + NS, kaddr(u), wave);
-        if (j + NS - 1 < n_tiles) ld.issue(ld.vbase, j + NS - 1, vaddr((u + NS - 1) % NS), wave);
+        if (j + NS < n_tiles) ld.issue(ld.kbase, ld.pkbase, j + NS, kaddr(u), wave);
+        if (j + NS - 1 < n_tiles) ld.issue(ld.vbase, ld.pvbase, j + NS - 1, vaddr((u + NS - 1) % NS), wave);
         if (j < my_tiles) {
             const lds_t *kn = kst((u + 1) % NS);   // past the last tile: an unused read
             const lds_t *vc = vst(u);
@@ -344,7 +406,7 @@ void prefill_bf16_kernel(PrefillArgs p) {
             for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) vf[cc * C::DB + db] = vt_frag<D>(vc, cc, db);
-            if (j >= n_full) mask_tile<D>(s, j * KT, qrow, L);
+            if (j >= n_full) mask_tile<D>(s, j * KT, P + qrow, P + L);
             tile_max<D>(s, c, st);
             apply_rescale<D>(st);
             tile_pv<D>(s, vf, c, st);
@@ -406,14 +468,14 @@ void prefill_bf16_kernel(PrefillArgs p) {
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int64_t grid, hipStream_t s) {
-    switch (head_dim) {
-    case 64:
-        hipLaunchKernelGGL((prefill_bf16_kernel<64>), dim3((unsigned)grid), dim3(NWAVE * 64), 0, s, a);
-        break;
-    case 128:
-        hipLaunchKernelGGL((prefill_bf16_kernel<128>), dim3((unsigned)grid), dim3(NWAVE * 64), 0, s, a);
-        break;
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int64_t grid, bool prefix,
+                               hipStream_t s) {
+    const dim3 g((unsigned)grid), b(NWAVE * 64);
+    switch (head_dim * 2 + (prefix ? 1 : 0)) {
+    case 128: hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), g, b, 0, s, a); break;
+    case 129: hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), g, b, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), g, b, 0, s, a); break;
+    case 257: hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), g, b, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
             const int32_t s = sigma[p - start[lo]], t = maxnb - 1 - lo;
             items[2 * p] = s;
             items[2 * p + 1] = t;
-            rec[p] = make_int4(cu[s], cu[s + 1] - cu[s], t, 0);
+            rec[p] = make_int4(cu[s], cu[s + 1] - cu[s], t, s);
         }
     } else {
         // qoff[r] = first item of the r-th question in that order.
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
             const int32_t t = nb - 1 - (p - qoff[lo]);
             items[2 * p] = s;
             items[2 * p + 1] = t;
-            rec[p] = make_int4(cu[s], cu[s + 1] - cu[s], t, 0);
+            rec[p] = make_int4(cu[s], cu[s + 1] - cu[s], t, s);
         }
     }
     if (tid == 0) ws[0] = n_items;
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64) void schedule_small_kernel(ScheduleArgs a) {
                 const int p = above + rank;
                 items[2 * p] = lane;
                 items[2 * p + 1] = t;
-                rec[p] = make_int4(q0, len, t, 0);
+                rec[p] = make_int4(q0, len, t, lane);
             }
             int c = 0;
             for (int j = 0; j < a.n_seg; ++j) c += __builtin_amdgcn_readlane(nb, j) > t ? 1 : 0;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(64) void schedule_small_kernel(ScheduleArgs a) {
             const int p = before + k, t = nb - 1 - k;
             items[2 * p] = lane;
             items[2 * p + 1] = t;
-            rec[p] = make_int4(q0, len, t, 0);
+            rec[p] = make_int4(q0, len, t, lane);
         }
     }
     if (lane == 0) ws[0] = n_items;

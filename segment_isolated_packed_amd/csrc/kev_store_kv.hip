@@ -3,7 +3,9 @@
 // Every question of a packed prefill gets a slot of the pre-allocated pool on
 // entry (Kev part 2, gsyq.cn, section 2.2), and its K and V rows become rows
 // 0..len-1 of that slot, written in place (primer, sakurs2.com, section 2.2),
-// so that decode can continue each question from its slot.
+// so that decode can continue each question from its slot.  For a chunk that
+// continues P rows already in its slot (chunked prefill), the rows go to
+// P..P+len-1 instead.
 //
 // The copy is pure data movement, bound by HBM: each workgroup moves 32 token
 // rows of one KV head for K and for V, 16 bytes per lane, whole rows per
@@ -41,17 +43,19 @@ __global__ __launch_bounds__(kThreads) void store_kv_kernel(StoreKvArgs a) {
         }
         const int s = lo;
         const int start = a.cu[s], len = a.cu[s + 1] - start;
-        const int pos = t - start;
+        const int i = t - start;
         const int slot = a.slot_ids[s];
+        const int P = a.prefix_lens ? a.prefix_lens[s] : 0;
         if (slot < 0 || slot >= a.n_slots) {
-            if (pos == 0 && chunk == 0 && g == 0) atomicOr(a.err, (int32_t)KEV_DEVERR_SLOT);
+            if (i == 0 && chunk == 0 && g == 0) atomicOr(a.err, (int32_t)KEV_DEVERR_SLOT);
             continue;
         }
-        if (len > a.capacity) {
-            if (pos == 0 && chunk == 0 && g == 0) atomicOr(a.err, (int32_t)KEV_DEVERR_CACHE_LEN);
+        if (P < 0 || len > a.capacity - P) {
+            if (i == 0 && chunk == 0 && g == 0) atomicOr(a.err, (int32_t)KEV_DEVERR_CACHE_LEN);
             continue;
         }
-        if (pos < 0 || pos >= len) continue;   // cu_seqlens not a valid partition (flagged by the prefill)
+        if (i < 0 || i >= len) continue;   // cu_seqlens not a valid partition (flagged by the prefill)
+        const int pos = P + i;
         const int64_t plane = (int64_t)a.capacity * D;
         uint16_t *kdst = static_cast<uint16_t *>(a.pool) + ((int64_t)slot * 2 * a.kv_heads + g) * plane +
                          (int64_t)pos * D + chunk * 8;

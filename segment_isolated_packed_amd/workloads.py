@@ -43,11 +43,14 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
-    x = rng.standard_normal(shape, dtype=np.float32)
-    return round_to_bf16_bits(x) if dtype == BF16 else x
+    if dtype != BF16:
+        return rng.standard_normal(shape, dtype=np.float32)
+    out = np.empty(shape, dtype=np.uint16)   # same draws as one call, in cache-sized pieces
+    _normal_into(rng, out.reshape(-1, shape[-1]) if len(shape) > 1 else out.reshape(-1, 1))
+    return out
 
 
-def _normal_into(rng: np.random.Generator, out: np.ndarray, chunk_rows: int = 1 << 14) -> None:
+def _normal_into(rng: np.random.Generator, out: np.ndarray, chunk_rows: int = 1 << 12) -> None:
     """Fill a bf16-bits array with N(0,1) draws, chunked along axis 0 to cap host memory."""
     flat = out.reshape(out.shape[0], -1)
     for lo in range(0, flat.shape[0], chunk_rows):
@@ -277,3 +280,84 @@ def make_decode(n_req: int = 64, n_slots: int = 80, capacity: int = 2458, heads:
     v_new = _normal(rng, (n_req, kv_heads, head_dim), dtype)
     return DecodeCase(name, dtype, heads, kv_heads, head_dim, n_slots, capacity, seed,
                       slot_ids, lens, q, k_new, v_new, pool)
+
+
+@dataclass
+class ChunkedCase:
+    """A packed batch of prompt chunks, each continuing the rows already cached in its slot."""
+    name: str
+    heads: int
+    kv_heads: int
+    head_dim: int
+    n_slots: int
+    capacity: int
+    seed: int
+    seqlens: np.ndarray      # chunk lengths
+    prefix_lens: np.ndarray  # int32 [n_seg], rows already in each slot
+    slot_ids: np.ndarray     # int32 [n_seg], distinct
+    q: np.ndarray            # [T, heads, d]     bf16 bits
+    k: np.ndarray            # [T, kv_heads, d]
+    v: np.ndarray            # [T, kv_heads, d]
+    pool: np.ndarray         # [n_slots, 2, kv_heads, capacity, d]
+    dtype: str = BF16
+    cu_seqlens: np.ndarray = field(init=False)
+
+    def __post_init__(self):
+        self.cu_seqlens = cu_from_lengths(self.seqlens)
+
+    @property
+    def n_seg(self) -> int:
+        return len(self.seqlens)
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    def effective_flops(self) -> int:
+        """Unmasked score entries only (chunk row i of a question with prefix P sees P + i + 1
+        keys): 2 FLOP per MAC for QK^T and again for PV."""
+        L = self.seqlens.astype(np.int64)
+        P = self.prefix_lens.astype(np.int64)
+        return int(4 * self.head_dim * self.heads * int((L * P + L * (L + 1) // 2).sum()))
+
+    def algorithmic_bytes(self) -> int:
+        """Compulsory HBM traffic: q, k, v and out of the chunk once, the prefix K/V rows
+        once, and the chunk's K/V rows written into the slots."""
+        T, d = self.total_tokens, self.head_dim
+        prefix = int(self.prefix_lens.astype(np.int64).sum())
+        return int(2 * d * (T * (2 * self.heads + 2 * self.kv_heads) + 2 * self.kv_heads * (prefix + T)))
+
+
+def make_chunked(seqlens, prefix_lens, heads: int, kv_heads: int, head_dim: int, capacity: int,
+                 n_slots: int, seed: int, name: str = "chunked") -> ChunkedCase:
+    """Chunked-prefill inputs (bf16).  Draw order: slot ids (first n_seg of a permutation of
+    the pool), the whole pool (every row filled, so rows past each prefix hold stale values a
+    correct kernel never reads), q, k, v of the chunks."""
+    seqlens = np.asarray(seqlens, dtype=np.int64)
+    prefix_lens = np.asarray(prefix_lens, dtype=np.int32)
+    if len(seqlens) != len(prefix_lens) or (prefix_lens + seqlens > capacity).any():
+        raise ValueError("every chunk must fit its slot after its prefix")
+    rng = np.random.default_rng(seed)
+    slot_ids = rng.permutation(n_slots)[:len(seqlens)].astype(np.int32)
+    pool = np.empty((n_slots, 2, kv_heads, capacity, head_dim), dtype=np.uint16)
+    _normal_into(rng, pool.reshape(-1, head_dim))
+    T = int(seqlens.sum())
+    q = _normal(rng, (T, heads, head_dim), BF16)
+    k = _normal(rng, (T, kv_heads, head_dim), BF16)
+    v = _normal(rng, (T, kv_heads, head_dim), BF16)
+    return ChunkedCase(name, heads, kv_heads, head_dim, n_slots, capacity, seed, seqlens, prefix_lens,
+                       slot_ids, q, k, v, pool)
+
+
+CHUNKED_DESCRIPTION = ("bf16, 28 q / 4 kv heads, head_dim 128 (Qwen2.5-7B attention shape): 8 prompts of "
+                       "8192 tokens prefilled in 2048-token chunks; the packed batch holds chunk s mod 4 of "
+                       "prompt s, so prefixes are 0, 2048, 4096, 6144 (twice each); 12-slot pool of capacity 8192")
+
+
+def chunked_case(seed: int = 46) -> ChunkedCase:
+    """The chunked-prefill workload: the batch a chunked scheduler would run once 8 long
+    prompts are spread over the four chunk phases (16384 new tokens against 24576 cached)."""
+    prefix = np.array([(s % 4) * 2048 for s in range(8)], np.int32)
+    return make_chunked([2048] * 8, prefix, 28, 4, 128, capacity=8192, n_slots=12, seed=seed,
+                        name="chunked_qwen25_7b")
+

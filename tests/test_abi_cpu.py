@@ -75,6 +75,28 @@ def test_prefill_slots_argument_checks(lib):
     assert _prefill_slots(lib, n_seg=-1) == K.KEV_ERR_INVALID_ARG
 
 
+def _chunked(lib, n_seg=2, kvh=4, d=128, n_slots=8, cap=64, pkvh=4, pd=128, dtype=0, null_pool=False,
+             null_ids=False, null_prefix=False, heads=8):
+    p = ctypes.c_void_p(16)
+    pool = K.KvPool(16, n_slots, cap, pkvh, pd, dtype)
+    return lib.kev_chunked_prefill_slots(p, p, p, p, n_seg, heads, kvh, d, p, 10,
+                                         None if null_pool else ctypes.byref(pool),
+                                         None if null_ids else p, None if null_prefix else p, None)
+
+
+def test_chunked_prefill_argument_checks(lib):
+    # every case fails on the host before any HIP call
+    assert _chunked(lib, null_pool=True) == K.KEV_ERR_INVALID_ARG
+    assert _chunked(lib, dtype=1) == K.KEV_ERR_UNSUPPORTED                # fp32 pool
+    assert _chunked(lib, pkvh=2) == K.KEV_ERR_INVALID_ARG                 # pool kv_heads differ
+    assert _chunked(lib, pd=64) == K.KEV_ERR_INVALID_ARG                  # pool head_dim differs
+    assert _chunked(lib, null_ids=True) == K.KEV_ERR_INVALID_ARG
+    assert _chunked(lib, null_prefix=True) == K.KEV_ERR_INVALID_ARG
+    assert _chunked(lib, n_seg=9) == K.KEV_ERR_BAD_SLOT                   # more questions than slots
+    assert _chunked(lib, d=16, pd=16) == K.KEV_ERR_UNSUPPORTED            # bf16 path: d 64 or 128
+    assert _chunked(lib, heads=6) == K.KEV_ERR_INVALID_ARG                # heads not a multiple of kv_heads
+
+
 def _decode(lib, n_req=4, heads=32, n_slots=8, cap=64, kvh=8, d=128, dtype=0, null=False):
     pool = K.KvPool(16, n_slots, cap, kvh, d, dtype)
     p = None if null else ctypes.c_void_p(16)
