@@ -5,8 +5,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 its binding, and the HIP path never imports it.
 
 ``kev_oracle.c`` holds the plain fp64 loops (full prefill, sampled prefill
-rows, slot-pool decode), the prefill-to-slot K/V store and chunked prefill
-against a slot prefix; ``dense.py`` holds the explicit dense-mask brute
+rows, slot-pool decode), the prefill-to-slot K/V store, chunked prefill
+against a slot prefix and decode against a paged (block-table) pool; ``dense.py`` holds the explicit dense-mask brute
 force for tiny inputs.  Each function cites the passage of the pages it
 follows in its own header comment or docstring.
 """
@@ -76,9 +76,11 @@ class Oracle:
         L.kev_oracle_decode.argtypes = [P, P, I, I, I, I, P, P, P, P, I, I, C, P, P, C]
         L.kev_oracle_store_kv.argtypes = [P, P, C, P, I, I, I, P, P, I, I, P]
         L.kev_oracle_chunked_prefill.argtypes = [P, P, P, C, P, I, I, I, I, P, P, P, I, I, P, P, C]
+        L.kev_oracle_paged_decode.argtypes = [P, P, I, I, I, I, P, I, P, P, P, I, I, C, P, P, C]
         L.kev_oracle_max_threads.argtypes = []
         for f in (L.kev_oracle_prefill, L.kev_oracle_prefill_rows, L.kev_oracle_decode,
-                  L.kev_oracle_store_kv, L.kev_oracle_chunked_prefill, L.kev_oracle_max_threads):
+                  L.kev_oracle_store_kv, L.kev_oracle_chunked_prefill, L.kev_oracle_paged_decode,
+                  L.kev_oracle_max_threads):
             f.restype = C
         self._L = L
         self.path = path
@@ -135,6 +137,28 @@ class Oracle:
         after = np.empty_like(pool) if want_pool else None
         self._check(self._L.kev_oracle_decode(
             _ptr(q), _ptr(pool), n_slots, capacity, kv_heads, d, _ptr(slot_ids),
+            _ptr(cache_lens), _ptr(k_new), _ptr(v_new), n_req, heads, _code(dtype), _ptr(out),
+            _ptr(after), n_threads))
+        return (out, after) if want_pool else out
+
+    def paged_decode(self, q, pool, block_tables, cache_lens, k_new, v_new, heads: int, dtype: str,
+                     want_pool: bool = False, n_threads: int = 0):
+        """Decode against a paged pool [n_blocks, 2, kv_heads, block_size, d] read through
+        block_tables [n_req, max_blocks]; returns out[n_req, heads, d] (fp64) and, if
+        ``want_pool``, the pool after the in-place append."""
+        q, pool, k_new, v_new = (_input(x, dtype) for x in (q, pool, k_new, v_new))
+        n_blocks, two, kv_heads, block_size, d = pool.shape
+        if two != 2:
+            raise ValueError("pool must be [n_blocks, 2, kv_heads, block_size, d]")
+        tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cache_lens = np.ascontiguousarray(cache_lens, dtype=np.int32)
+        n_req = len(cache_lens)
+        if tables.ndim != 2 or tables.shape[0] != n_req:
+            raise OracleError(-1)
+        out = np.zeros((n_req, heads, d), dtype=np.float64)
+        after = np.empty_like(pool) if want_pool else None
+        self._check(self._L.kev_oracle_paged_decode(
+            _ptr(q), _ptr(pool), n_blocks, block_size, kv_heads, d, _ptr(tables), tables.shape[1],
             _ptr(cache_lens), _ptr(k_new), _ptr(v_new), n_req, heads, _code(dtype), _ptr(out),
             _ptr(after), n_threads))
         return (out, after) if want_pool else out

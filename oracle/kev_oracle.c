@@ -534,3 +534,116 @@ int kev_oracle_chunked_prefill(const void *q, const void *k, const void *v, int 
     }
     return ORACLE_OK;
 }
+
+/*
+ * Decode against a paged KV pool (primer, sakurs2.com, section 2.5): the cache is cut into
+ * fixed-size blocks of `block_size` positions that can sit anywhere in the pool, and request
+ * r finds its position p in block block_tables[r][p / block_size], row p % block_size.  Apart
+ * from where the rows live, the step is the slot decode above: the new K/V row is written in
+ * place at position L-1 (section 2.2), and the query attends over positions 0..L-1.
+ *   pool[n_blocks][2][kv_heads][block_size][d]; block_tables[n_req][max_blocks];
+ *   positions 0..L-2 are read before any append of the call.  Blocks may be shared between
+ *   requests for reading; an append target (block, row) must be touched by no other request.
+ */
+static int paged_row_taken(const int32_t *bt, int32_t max_blocks, const int32_t *lens, int32_t n_req,
+                           int32_t bs, int32_t r, int32_t blk, int32_t row)
+{
+    for (int32_t r2 = 0; r2 < n_req; r2++) {
+        if (r2 == r)
+            continue;
+        /* request r2 reads rows 0..L2-2 and writes row L2-1 */
+        for (int32_t p = 0; p < lens[r2]; p++)
+            if (bt[(size_t)r2 * max_blocks + p / bs] == blk && p % bs == row)
+                return 1;
+    }
+    return 0;
+}
+
+int kev_oracle_paged_decode(const void *q, const void *pool, int32_t n_blocks, int32_t block_size,
+                            int32_t kv_heads, int32_t d, const int32_t *block_tables, int32_t max_blocks,
+                            const int32_t *cache_lens, const void *k_new, const void *v_new, int32_t n_req,
+                            int32_t heads, int dtype, double *out, void *pool_after, int n_threads)
+{
+    int rc = check_heads(heads, kv_heads, d, dtype);
+    if (rc)
+        return rc;
+    if (n_req < 0 || n_blocks <= 0 || block_size <= 0 || max_blocks <= 0)
+        return ORACLE_BAD_ARG;
+    for (int32_t r = 0; r < n_req; r++) {
+        int32_t L = cache_lens[r];
+        if (L < 1 || (L - 1) / block_size >= max_blocks)
+            return ORACLE_SLOT_OVERFLOW;
+        for (int32_t j = 0; j <= (L - 1) / block_size; j++) {
+            int32_t b = block_tables[(size_t)r * max_blocks + j];
+            if (b < 0 || b >= n_blocks)
+                return ORACLE_BAD_SLOT;
+        }
+        int32_t last = block_tables[(size_t)r * max_blocks + (L - 1) / block_size];
+        if (paged_row_taken(block_tables, max_blocks, cache_lens, n_req, block_size, r, last,
+                            (L - 1) % block_size))
+            return ORACLE_BAD_SLOT;
+    }
+    size_t esz = dtype == ORACLE_F32 ? 4 : 2;
+    size_t head_rows = (size_t)block_size * d;              /* one (block, K|V, head) */
+    size_t block_elems = (size_t)2 * kv_heads * head_rows;
+    int32_t cap = max_blocks * block_size;
+    int G = heads / kv_heads;
+    long units = (long)n_req * heads;
+    int fail = 0;
+    put_threads(n_threads);
+#pragma omp parallel
+    {
+        double *kbuf = malloc(sizeof(double) * (size_t)cap * d);
+        double *vbuf = malloc(sizeof(double) * (size_t)cap * d);
+        double *qv = malloc(sizeof(double) * d);
+        double *w = malloc(sizeof(double) * cap);
+        if (!kbuf || !vbuf || !qv || !w) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long u = 0; u < units; u++) {
+                const int32_t r = (int32_t)(u / heads), h = (int32_t)(u % heads);
+                const int32_t g = h / G;
+                int32_t L = cache_lens[r];
+                const int32_t *table = block_tables + (size_t)r * max_blocks;
+                for (int32_t p = 0; p < L - 1; p++) {
+                    size_t at = (size_t)table[p / block_size] * block_elems + (size_t)g * head_rows +
+                                (size_t)(p % block_size) * d;
+                    for (int32_t c = 0; c < d; c++) {
+                        kbuf[(size_t)p * d + c] = widen(pool, dtype, at + c);
+                        vbuf[(size_t)p * d + c] = widen(pool, dtype, at + (size_t)kv_heads * head_rows + c);
+                    }
+                }
+                for (int32_t c = 0; c < d; c++) {
+                    size_t src = ((size_t)r * kv_heads + g) * d + c, last = (size_t)(L - 1) * d + c;
+                    kbuf[last] = widen(k_new, dtype, src);
+                    vbuf[last] = widen(v_new, dtype, src);
+                    qv[c] = widen(q, dtype, ((size_t)r * heads + h) * d + c);
+                }
+                attend(qv, kbuf, vbuf, L, d, w, out + ((size_t)r * heads + h) * d);
+            }
+        }
+        free(kbuf);
+        free(vbuf);
+        free(qv);
+        free(w);
+    }
+    if (fail)
+        return ORACLE_NO_MEMORY;
+    if (pool_after) {
+        memcpy(pool_after, pool, esz * block_elems * (size_t)n_blocks);
+        for (int32_t r = 0; r < n_req; r++) {
+            int32_t p = cache_lens[r] - 1;
+            int32_t blk = block_tables[(size_t)r * max_blocks + p / block_size];
+            for (int32_t g = 0; g < kv_heads; g++) {
+                size_t kat = (size_t)blk * block_elems + (size_t)g * head_rows + (size_t)(p % block_size) * d;
+                size_t vat = kat + (size_t)kv_heads * head_rows;
+                size_t from = ((size_t)r * kv_heads + g) * d;
+                memcpy((char *)pool_after + kat * esz, (const char *)k_new + from * esz, esz * d);
+                memcpy((char *)pool_after + vat * esz, (const char *)v_new + from * esz, esz * d);
+            }
+        }
+    }
+    return ORACLE_OK;
+}

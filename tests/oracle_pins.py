@@ -404,4 +404,53 @@ def pin_chunked_prefill_against_slot_prefix(orc: oracle.Oracle):
     assert np.array_equal(pool, full_pool)
 
 
+def _paged_from_slots(pool, block_size, rng):
+    """Scatter every slot's rows into blocks of `block_size` positions at shuffled places of a
+    paged pool; returns the paged pool and each slot's block list."""
+    n_slots, two, kvh, cap, d = pool.shape
+    per = cap // block_size
+    perm = rng.permutation(n_slots * per)
+    paged = np.zeros((n_slots * per, 2, kvh, block_size, d), dtype=pool.dtype)
+    blocks = perm.reshape(n_slots, per)
+    for s_ in range(n_slots):
+        for j in range(per):
+            paged[blocks[s_, j]] = pool[s_, :, :, j * block_size:(j + 1) * block_size]
+    return paged, blocks
+
+
+def pin_paged_decode_equals_slot_decode(orc: oracle.Oracle):
+    """Primer section 2.5: a paged cache stores the same K/V rows in fixed-size blocks placed
+    anywhere and found through a block table, so decoding through the table must give the slot
+    decode's result bit for bit (sections 2.2/2.4: same rows, same order, same arithmetic), and
+    the append must land in the block and row that hold position L-1.  Blocks shared between
+    requests for reading (a common prefix) are read by both."""
+    rng = np.random.default_rng(71)
+    n_slots, kvh, cap, d, hq = 6, 2, 24, 16, 8
+    pool = _bf16(rng.standard_normal((n_slots, 2, kvh, cap, d)))
+    for bs in (4, 8, 24):
+        paged, blocks = _paged_from_slots(pool, bs, rng)
+        ids = np.array([4, 0, 2, 5, 1], np.int32)
+        lens = np.array([1, bs, min(bs + 1, cap), cap, 7], np.int32)   # first row, block edges, full slot
+        qn, kn, vn = (_bf16(rng.standard_normal((5, h, d))) for h in (hq, kvh, kvh))
+        ref, ref_pool = orc.decode(qn, pool, ids, lens, kn, vn, hq, W.BF16, want_pool=True)
+        tables = blocks[ids]
+        out, after = orc.paged_decode(qn, paged, tables, lens, kn, vn, hq, W.BF16, want_pool=True)
+        assert np.array_equal(out, ref), bs
+        for s_ in range(n_slots):      # gather the paged pool back into slot order
+            for j in range(cap // bs):
+                assert np.array_equal(after[blocks[s_, j]], ref_pool[s_, :, :, j * bs:(j + 1) * bs])
+    # two requests share their first two blocks read-only and append into blocks of their own
+    bs = 4
+    paged, blocks = _paged_from_slots(pool, bs, rng)
+    tables = np.stack([blocks[1], blocks[1].copy()])
+    tables[1, 2:] = blocks[3, :tables.shape[1] - 2]
+    lens = np.array([10, 11], np.int32)
+    qn, kn, vn = (_bf16(rng.standard_normal((2, h, d))) for h in (hq, kvh, kvh))
+    out = orc.paged_decode(qn, paged, tables, lens, kn, vn, hq, W.BF16)
+    # the same rows laid out as two private slots
+    priv = np.stack([pool[1], pool[1].copy()])
+    priv[1, :, :, 8:] = pool[3, :, :, :cap - 8]
+    assert np.array_equal(out, orc.decode(qn, priv, [0, 1], lens, kn, vn, hq, W.BF16))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -48,6 +48,14 @@ MUTANTS = {
     "chunk_rows_overwrite_prefix": ("kbuf[(size_t)(P + j) * d + c] = widen(k, dtype, src);",
                                     "kbuf[(size_t)j * d + c] = widen(k, dtype, src);"),
     "chunk_stored_at_row_zero": ("size_t row = (size_t)(prefix_lens[s] + i - cu[s]);", "size_t row = (size_t)(i - cu[s]);"),
+    "paged_block_of_next_position": ("size_t at = (size_t)table[p / block_size] * block_elems",
+                                     "size_t at = (size_t)table[(p + 1) / block_size] * block_elems"),
+    "paged_row_ignores_block_offset": ("(size_t)(p % block_size) * d;\n                    for",
+                                       "(size_t)(p / block_size) * d;\n                    for"),
+    "paged_v_from_k_plane": ("vbuf[(size_t)p * d + c] = widen(pool, dtype, at + (size_t)kv_heads * head_rows + c);",
+                             "vbuf[(size_t)p * d + c] = widen(pool, dtype, at + c);"),
+    "paged_append_into_first_block": ("int32_t blk = block_tables[(size_t)r * max_blocks + p / block_size];",
+                                      "int32_t blk = block_tables[(size_t)r * max_blocks];"),
     "append_k_into_v_plane": (
         "memcpy((char *)pool_after + kdst * esz, (const char *)k_new + src * esz, esz * d);",
         "memcpy((char *)pool_after + vdst * esz, (const char *)k_new + src * esz, esz * d);"),
