@@ -10,8 +10,9 @@ Prints ONE JSON line.  `value` is the prefill's effective TFLOP/s (only unmasked
 entries counted: 4 * d * heads * sum L(L+1)/2 FLOPs per call) over the average duration
 of the prefill call measured with HIP events on the launch stream.  The decode's
 achieved HBM GB/s (algorithmic bytes over event-timed duration) is reported beside it,
-and so are two more calls timed the same way: the prefill that also stores every question's
-K/V into its slot, and a chunked prefill of 8 long prompts against their cached prefixes.
+and so are more calls timed the same way: the prefill that also stores every question's K/V
+into its slot, a chunked prefill of 8 long prompts against their cached prefixes, and the
+decode over a paged (block-table) pool holding the same rows.
 """
 from __future__ import annotations
 
@@ -201,6 +202,39 @@ def main():
         slots_res = {"ms": slots_ms, "store_bytes": store_bytes, "slot_capacity": cap}
         del spool
 
+    # The decode over a paged pool (kev_paged_attn_decode): the same requests and rows cut into
+    # blocks of B positions scattered over a pool of only the blocks the lengths need.
+    paged_res = []
+    if do_dec:
+        for B in (16, 64):
+            log(f"paged decode, block size {B}")
+            pg = W.paged_from_slots(dc, B)
+            ppool, pq, pkn, pvn = (to_dev(x, W.BF16) for x in (pg.pool, pg.q, pg.k_new, pg.v_new))
+            ptab, plen = (torch.from_numpy(x).to(dev) for x in (pg.block_tables, pg.cache_lens))
+            pout = torch.empty_like(pq)
+            pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+            for i in range(max(args.warmup, 1) + args.steps):
+                if args.flush == "read":
+                    torch.sum(flush_rows, dim=1, dtype=torch.int32, out=flush_sink)
+                elif args.flush == "write":
+                    flush_buf.fill_(1)
+                e = pev[i - max(args.warmup, 1)] if i >= max(args.warmup, 1) else None
+                if e: e[0].record(stream)
+                K.kev_paged_attn_decode(pq, ppool, ptab, plen, pkn, pvn, out=pout)
+                if e: e[1].record(stream)
+            torch.cuda.synchronize()
+            if K.kev_get_device_errors():
+                raise RuntimeError("device error flags in the paged-decode leg")
+            ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
+            reserved = pg.n_blocks * B
+            paged_res.append({
+                "block_size": B, "ms": ms, "gbps": pg.algorithmic_bytes() / (ms * 1e-3) / 1e9,
+                "algorithmic_mb": pg.algorithmic_bytes() / 1e6, "blocks": pg.n_blocks,
+                "pool_mb": pg.pool.nbytes / 1e6, "slot_pool_mb": dc.pool.nbytes / 1e6,
+                "rows_used": int(dc.cache_lens.sum()), "rows_reserved_paged": reserved,
+                "rows_reserved_slots": dc.n_slots * dc.capacity})
+            del ppool, pq, pkn, pvn, pout
+
     # Chunked prefill against slot prefixes (kev_chunked_prefill_slots) on its own workload:
     # 8 long prompts at four different chunk phases, packed into one call.
     chunk_res = None
@@ -288,6 +322,7 @@ def main():
             "store_gbps_incl_launch": slots_res["store_bytes"] / max(slots_res["ms"] - pre_avg, 1e-6) / 1e6,
             "call": "kev_packed_attn_prefill_slots: prefill + every question's K/V stored into its slot"},
         "chunked_prefill": chunk_res,
+        "paged_decode": paged_res or None,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and do_pre:

@@ -29,6 +29,9 @@
  *       cached in its slot; the chunk attends to them and to itself causally,
  *       and its K/V rows are appended to the slot.
  *
+ *   kev_paged_attn_decode  the decode step against a paged pool: fixed-size
+ *       blocks placed anywhere, found through per-request block tables.
+ *
  * Conventions shared by every call
  *   - Tensor pointers are DEVICE pointers owned by the caller, contiguous in
  *     the layouts stated below, never freed or retained by the library.
@@ -75,6 +78,7 @@ typedef enum {
 #define KEV_DEVERR_SEQLENS 1u   /* cu_seqlens invalid; the prefill call computed nothing */
 #define KEV_DEVERR_SLOT 2u      /* a request's slot id was out of range; request skipped */
 #define KEV_DEVERR_CACHE_LEN 4u /* a request's cache length was outside [1, capacity]; skipped */
+#define KEV_DEVERR_BLOCK 8u     /* a paged request's block id was outside the pool; skipped */
 
 /*
  * Packed, segment-isolated causal prefill.
@@ -139,6 +143,56 @@ int kev_slot_attn_decode(const void *q, const kev_kv_pool *kv_pool,
                          const int32_t *slot_ids, const int32_t *cache_lens, void *out,
                          const void *k_new, const void *v_new, int32_t n_req, int32_t heads,
                          void *stream);
+
+/*
+ * Paged KV pool: n_blocks blocks of block_size positions each, stored as
+ * [n_blocks][2][kv_heads][block_size][head_dim] (per block and KV head, the
+ * block's K rows then, kv_heads*block_size*head_dim elements later, its V
+ * rows).  A block is a slot of capacity block_size; blocks are handed out on
+ * demand and may sit anywhere (primer, sakurs2.com, section 2.5).
+ */
+typedef struct kev_paged_pool {
+    void *data;         /* device pointer */
+    int32_t n_blocks;
+    int32_t block_size; /* a power of two */
+    int32_t kv_heads;
+    int32_t head_dim;
+    int32_t dtype;      /* kev_dtype; KEV_BF16 only */
+} kev_paged_pool;
+
+/* Most blocks one paged decode request may span (block ids are staged on chip). */
+#define KEV_PAGED_MAX_BLOCKS 2048
+
+/*
+ * Single-token decode over a paged pool, with in-kernel append: the step of
+ * kev_slot_attn_decode, with position p of request r found in block
+ * block_tables[r * max_blocks + p / block_size], row p % block_size, rather
+ * than in a contiguous slot (primer, sakurs2.com, section 2.5: the attention
+ * reads K/V through the block table, without first gathering them into one
+ * contiguous span).  Row L-1 (L = cache_lens[r]) of that mapping is
+ * overwritten with k_new[r] / v_new[r] in place (same page, section 2.2), and
+ * query r attends over positions 0..L-1 with no mask.
+ *
+ *   q            [n_req, heads, head_dim]          bf16
+ *   kv_pool      host pointer to the paged pool descriptor
+ *   block_tables int32 [n_req, max_blocks], device; entries 0..(L-1)/block_size
+ *                of row r are block ids in [0, n_blocks), the rest are not read
+ *   cache_lens   int32 [n_req], device; positions AFTER the append, in
+ *                [1, min(max_blocks, KEV_PAGED_MAX_BLOCKS) * block_size]
+ *   out          [n_req, heads, head_dim]          bf16
+ *   k_new, v_new [n_req, kv_heads, head_dim]       bf16
+ *
+ * Blocks may be shared between requests for reading (a common prefix), but
+ * the row a request appends must be read or written by no other request of
+ * the call (rejected with KEV_ERR_BAD_SLOT under KEV_CHECK=1; undefined
+ * otherwise).  A request with a block id outside the pool, or a length out
+ * of range, is skipped (KEV_DEVERR_BLOCK / KEV_DEVERR_CACHE_LEN).  head_dim
+ * must be 64 or 128 and at most 32 query heads may share a KV head.
+ */
+int kev_paged_attn_decode(const void *q, const kev_paged_pool *kv_pool, const int32_t *block_tables,
+                          int32_t max_blocks, const int32_t *cache_lens, void *out,
+                          const void *k_new, const void *v_new, int32_t n_req, int32_t heads,
+                          void *stream);
 
 /*
  * Packed prefill that also hands each question its slot: the prefill above,

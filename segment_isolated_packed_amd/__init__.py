@@ -23,7 +23,8 @@ KEV_ERR_SLOT_OVERFLOW = -4
 KEV_ERR_BAD_SLOT = -5
 KEV_ERR_DEVICE = -6
 KEV_ERR_NO_MEMORY = -7
-KEV_DEVERR_SEQLENS, KEV_DEVERR_SLOT, KEV_DEVERR_CACHE_LEN = 1, 2, 4
+KEV_DEVERR_SEQLENS, KEV_DEVERR_SLOT, KEV_DEVERR_CACHE_LEN, KEV_DEVERR_BLOCK = 1, 2, 4, 8
+KEV_PAGED_MAX_BLOCKS = 2048
 KEV_ORDER_QUESTION, KEV_ORDER_LEVEL = 0, 1
 
 
@@ -36,6 +37,12 @@ class KevError(RuntimeError):
 class KvPool(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("n_slots", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class PagedPool(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("n_blocks", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
@@ -61,6 +68,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kev_slot_attn_decode.argtypes = [P, ctypes.POINTER(KvPool), P, P, P, P, P, I, I, P]
     L.kev_packed_attn_prefill_slots.argtypes = [P, P, P, P, I, I, I, I, P, I, ctypes.POINTER(KvPool), P, P]
     L.kev_chunked_prefill_slots.argtypes = [P, P, P, P, I, I, I, I, P, I, ctypes.POINTER(KvPool), P, P, P]
+    L.kev_paged_attn_decode.argtypes = [P, ctypes.POINTER(PagedPool), P, I, P, P, P, P, I, I, P]
     L.kev_status_string.argtypes = [ctypes.c_int]
     L.kev_status_string.restype = ctypes.c_char_p
     L.kev_get_device_errors.argtypes = [P, ctypes.POINTER(I)]
@@ -69,7 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kev_schedule_host.argtypes = [P, I, I, I, P, I, ctypes.POINTER(I)]
     L.kev_schedule_device.argtypes = [P, I, I, I, I, P, I, ctypes.POINTER(I), P]
     for f in (L.kev_packed_attn_prefill, L.kev_slot_attn_decode, L.kev_packed_attn_prefill_slots,
-              L.kev_chunked_prefill_slots, L.kev_get_device_errors,
+              L.kev_chunked_prefill_slots, L.kev_paged_attn_decode, L.kev_get_device_errors,
               L.kev_prefill_block_rows, L.kev_prefill_order, L.kev_schedule_host,
               L.kev_schedule_device):
         f.restype = ctypes.c_int
@@ -169,6 +177,39 @@ def kev_slot_attn_decode(q, kv_pool, slot_ids, cache_lens, k_new, v_new, out=Non
                                 _dev_ptr(out, "out"), _dev_ptr(k_new, "k_new"),
                                 _dev_ptr(v_new, "v_new"), n_req, heads, _stream(stream))
     _check(rc, "kev_slot_attn_decode")
+    return out
+
+
+def kev_paged_attn_decode(q, kv_pool, block_tables, cache_lens, k_new, v_new, out=None, stream=None):
+    """Single-token decode with in-kernel append into a paged pool.
+
+    q [n_req, heads, d]; kv_pool [n_blocks, 2, kv_heads, block_size, d] (bf16, updated in
+    place); block_tables int32 [n_req, max_blocks] and cache_lens int32 [n_req] on the
+    device; k_new / v_new [n_req, kv_heads, d].  Returns out [n_req, heads, d].
+    """
+    import torch
+    L = load_library()
+    n_req, heads, d = q.shape
+    n_blocks, two, kv_heads, block_size, pd = kv_pool.shape
+    if two != 2 or pd != d:
+        raise ValueError("kv_pool must be [n_blocks, 2, kv_heads, block_size, head_dim]")
+    if k_new.shape != (n_req, kv_heads, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [n_req, kv_heads, head_dim]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != n_req:
+        raise ValueError("block_tables must be int32 [n_req, max_blocks]")
+    if cache_lens.dtype != torch.int32 or cache_lens.numel() != n_req:
+        raise ValueError("cache_lens must be int32 [n_req]")
+    for t in (kv_pool, k_new, v_new):
+        if t.dtype != q.dtype:
+            raise TypeError("q, kv_pool, k_new, v_new must share one dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    pool = PagedPool(_dev_ptr(kv_pool, "kv_pool").value, n_blocks, block_size, kv_heads, d,
+                     _dtype_code(kv_pool))
+    rc = L.kev_paged_attn_decode(_dev_ptr(q, "q"), ctypes.byref(pool), _dev_ptr(block_tables, "block_tables"),
+                                 block_tables.shape[1], _dev_ptr(cache_lens, "cache_lens"), _dev_ptr(out, "out"),
+                                 _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"), n_req, heads, _stream(stream))
+    _check(rc, "kev_paged_attn_decode")
     return out
 
 

@@ -271,6 +271,69 @@ int store_rows(const void *k, const void *v, const int32_t *cu_seqlens, int32_t 
     return to_status(launch_store_kv(sa, head_dim, stream));
 }
 
+// Decode shapes the kernel covers: bf16, head_dim 64 or 128, up to 32 query heads per KV head
+// (they are the columns of one MFMA tile).
+int check_decode_shape(int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype) {
+    if (heads % kv_heads != 0) return KEV_ERR_INVALID_ARG;
+    if (dtype != KEV_BF16) return KEV_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return KEV_ERR_UNSUPPORTED;
+    if (heads / kv_heads > 32) return KEV_ERR_UNSUPPORTED;
+    return KEV_OK;
+}
+
+// KEV_CHECK for a paged decode: cache lengths in range, the block ids a request reads inside
+// the pool, and every append target (block, row) touched by no other request of the call.
+int host_check_paged(const std::vector<int32_t> &tables, const std::vector<int32_t> &lens, int32_t max_blocks,
+                     int32_t n_blocks, int32_t bs) {
+    const int32_t n_req = (int32_t)lens.size();
+    const int64_t limit = std::min<int64_t>(max_blocks, KEV_PAGED_MAX_BLOCKS) * (int64_t)bs;
+    std::vector<char> appended((size_t)n_blocks * bs, 0);
+    for (int32_t r = 0; r < n_req; ++r) {
+        if (lens[r] < 1 || lens[r] > limit) return KEV_ERR_SLOT_OVERFLOW;
+        for (int32_t j = 0; j <= (lens[r] - 1) / bs; ++j) {
+            const int32_t b = tables[(size_t)r * max_blocks + j];
+            if (b < 0 || b >= n_blocks) return KEV_ERR_BAD_SLOT;
+        }
+        const int32_t p = lens[r] - 1;
+        char &a = appended[(size_t)tables[(size_t)r * max_blocks + p / bs] * bs + p % bs];
+        if (a) return KEV_ERR_BAD_SLOT;
+        a = 1;
+    }
+    for (int32_t r = 0; r < n_req; ++r)
+        for (int32_t p = 0; p + 1 < lens[r]; ++p)
+            if (appended[(size_t)tables[(size_t)r * max_blocks + p / bs] * bs + p % bs]) return KEV_ERR_BAD_SLOT;
+    return KEV_OK;
+}
+
+// Launch a decode (slot or paged pool) once the pool-specific fields of `da` are set.
+int run_decode(DecodeArgs &da, const void *q, void *data, int32_t kv_heads, int32_t head_dim,
+               const int32_t *cache_lens, void *out, const void *k_new, const void *v_new, int32_t n_req,
+               int32_t heads, bool paged, hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
+    int rc = error_word(dev, &da.err);
+    if (rc) return rc;
+    da.q = q;
+    da.pool = data;
+    da.cache_lens = cache_lens;
+    da.out = out;
+    da.k_new = k_new;
+    da.v_new = v_new;
+    da.n_req = n_req;
+    da.heads = heads;
+    da.kv_heads = kv_heads;
+    da.group = heads / kv_heads;
+    da.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    if ((int64_t)n_req * kv_heads > INT32_MAX) return KEV_ERR_INVALID_ARG;
+    // Longest units first when the grid does not fit the CUs at once (two workgroups each);
+    // otherwise every workgroup starts at once and the order does not matter.
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return KEV_ERR_DEVICE;
+    da.ranked = (n_req <= 64 && (int64_t)n_req * kv_heads > 2 * (int64_t)cus) ? 1 : 0;
+    return to_status(launch_decode_bf16(da, head_dim, paged, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -281,8 +344,8 @@ const char *kev_status_string(int status) {
     case KEV_ERR_INVALID_ARG: return "invalid argument";
     case KEV_ERR_UNSUPPORTED: return "unsupported dtype/head_dim combination";
     case KEV_ERR_BAD_SEQLENS: return "cu_seqlens must start at 0, be non-decreasing and end at total_tokens";
-    case KEV_ERR_SLOT_OVERFLOW: return "cache length (or prefix plus chunk rows) outside the slot capacity";
-    case KEV_ERR_BAD_SLOT: return "slot id out of range or repeated";
+    case KEV_ERR_SLOT_OVERFLOW: return "cache length (or prefix plus chunk rows) outside the slot or block-table capacity";
+    case KEV_ERR_BAD_SLOT: return "slot or block id out of range, or repeated";
     case KEV_ERR_DEVICE: return "HIP runtime error";
     case KEV_ERR_NO_MEMORY: return "workspace allocation failed";
     default: return "unknown status";
@@ -347,10 +410,8 @@ int kev_slot_attn_decode(const void *q, const kev_kv_pool *pool, const int32_t *
     if (!pool || n_req < 0 || heads <= 0) return KEV_ERR_INVALID_ARG;
     if (pool->n_slots <= 0 || pool->capacity <= 0 || pool->kv_heads <= 0 || pool->head_dim <= 0)
         return KEV_ERR_INVALID_ARG;
-    if (heads % pool->kv_heads != 0) return KEV_ERR_INVALID_ARG;
-    if (pool->dtype != KEV_BF16) return KEV_ERR_UNSUPPORTED;
-    if (pool->head_dim != 64 && pool->head_dim != 128) return KEV_ERR_UNSUPPORTED;
-    if (heads / pool->kv_heads > 32) return KEV_ERR_UNSUPPORTED;   // query heads per KV head = MFMA columns
+    int rc = check_decode_shape(heads, pool->kv_heads, pool->head_dim, pool->dtype);
+    if (rc) return rc;
     if (n_req == 0) return KEV_OK;
     if (n_req > pool->n_slots) return KEV_ERR_BAD_SLOT;
     if (!q || !pool->data || !slot_ids || !cache_lens || !out || !k_new || !v_new)
@@ -370,37 +431,46 @@ int kev_slot_attn_decode(const void *q, const kev_kv_pool *pool, const int32_t *
             if (lens[r] < 1 || lens[r] > pool->capacity) return KEV_ERR_SLOT_OVERFLOW;
         }
     }
-
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
-    int32_t *err = nullptr;
-    int rc = error_word(dev, &err);
-    if (rc) return rc;
-
     DecodeArgs da{};
-    da.q = q;
-    da.pool = pool->data;
     da.slot_ids = slot_ids;
-    da.cache_lens = cache_lens;
-    da.out = out;
-    da.k_new = k_new;
-    da.v_new = v_new;
-    da.n_req = n_req;
-    da.heads = heads;
-    da.kv_heads = pool->kv_heads;
-    da.group = heads / pool->kv_heads;
     da.n_slots = pool->n_slots;
     da.capacity = pool->capacity;
-    da.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pool->head_dim));
-    da.err = err;
-    if ((int64_t)n_req * pool->kv_heads > INT32_MAX) return KEV_ERR_INVALID_ARG;
-    // Longest units first when the grid does not fit the CUs at once (two workgroups each);
-    // otherwise every workgroup starts at once and the order does not matter.
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-        return KEV_ERR_DEVICE;
-    da.ranked = (n_req <= 64 && (int64_t)n_req * pool->kv_heads > 2 * (int64_t)cus) ? 1 : 0;
-    return to_status(launch_decode_bf16(da, pool->head_dim, stream));
+    return run_decode(da, q, pool->data, pool->kv_heads, pool->head_dim, cache_lens, out, k_new, v_new, n_req,
+                      heads, false, stream);
+}
+
+int kev_paged_attn_decode(const void *q, const kev_paged_pool *pool, const int32_t *block_tables,
+                          int32_t max_blocks, const int32_t *cache_lens, void *out, const void *k_new,
+                          const void *v_new, int32_t n_req, int32_t heads, void *stream_) {
+    if (!pool || n_req < 0 || heads <= 0 || max_blocks <= 0) return KEV_ERR_INVALID_ARG;
+    if (pool->n_blocks <= 0 || pool->kv_heads <= 0 || pool->head_dim <= 0) return KEV_ERR_INVALID_ARG;
+    const int32_t bs = pool->block_size;
+    if (bs <= 0 || (bs & (bs - 1)) != 0) return KEV_ERR_INVALID_ARG;   // a power of two
+    int rc = check_decode_shape(heads, pool->kv_heads, pool->head_dim, pool->dtype);
+    if (rc) return rc;
+    if (n_req == 0) return KEV_OK;
+    if (!q || !pool->data || !block_tables || !cache_lens || !out || !k_new || !v_new)
+        return KEV_ERR_INVALID_ARG;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+
+    if (check_enabled()) {
+        std::vector<int32_t> tables((size_t)n_req * max_blocks), lens(n_req);
+        if (hipMemcpyAsync(tables.data(), block_tables, sizeof(int32_t) * tables.size(), hipMemcpyDeviceToHost,
+                           stream) != hipSuccess ||
+            hipMemcpyAsync(lens.data(), cache_lens, sizeof(int32_t) * n_req, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess)
+            return KEV_ERR_DEVICE;
+        rc = host_check_paged(tables, lens, max_blocks, pool->n_blocks, bs);
+        if (rc) return rc;
+    }
+    DecodeArgs da{};
+    da.n_slots = pool->n_blocks;
+    da.capacity = bs;
+    da.block_tables = block_tables;
+    da.max_blocks = max_blocks;
+    da.block_shift = __builtin_ctz((unsigned)bs);
+    return run_decode(da, q, pool->data, pool->kv_heads, pool->head_dim, cache_lens, out, k_new, v_new, n_req,
+                      heads, true, stream);
 }
 
 int kev_get_device_errors(void *stream_, int32_t *flags_out) {

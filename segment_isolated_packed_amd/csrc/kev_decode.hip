@@ -32,6 +32,15 @@
 //   - when there are more units than the CUs hold at once (and at most 64
 //     requests), workgroups are issued longest unit first, so the short units
 //     fill in at the end.
+//
+// Paged variant (the PAGED instantiation).  The cache may instead be cut into
+// fixed-size blocks of B positions placed anywhere in the pool, request r
+// finding position p in block block_tables[r][p / B], row p % B (primer,
+// section 2.5: blocks allocated on demand and read through a block table, not
+// copied into one contiguous span first).  A block holds, per KV head, B K
+// rows then B V rows, i.e. it is a slot of capacity B.  The workgroup first
+// copies the request's block ids into LDS (checking them), then every row
+// address of a tile is looked up there; the rest of the kernel is unchanged.
 #include "kev_internal.h"
 #include "kev_mfma_core.h"
 #include "../../include/kev.h"
@@ -45,7 +54,9 @@ using namespace core;
 constexpr int DKT = 32;        // positions per tile
 constexpr int kWaves = 4;      // wavefronts per workgroup (one unit)
 
+template <bool PAGED>
 __device__ inline bool req_valid(int slot, int L, const DecodeArgs &p) {
+    if constexpr (PAGED) return L >= 1 && ((L - 1) >> p.block_shift) < min(p.max_blocks, kDecodeMaxBlocks);
     return slot >= 0 && slot < p.n_slots && L >= 1 && L <= p.capacity;
 }
 
@@ -55,13 +66,14 @@ __device__ inline bool req_valid(int slot, int L, const DecodeArgs &p) {
 struct Req {
     int r, slot, L;
 };
+template <bool PAGED>
 __device__ inline Req ranked_request(int b_req, const DecodeArgs &p) {
     const int lane = threadIdx.x & 63;
     int t = -1, sl = 0, ln = 0;
     if (lane < p.n_req) {
-        sl = p.slot_ids[lane];
+        sl = PAGED ? 0 : p.slot_ids[lane];
         ln = p.cache_lens[lane];
-        t = req_valid(sl, ln, p) ? (ln + DKT - 1) / DKT : 0;
+        t = req_valid<PAGED>(sl, ln, p) ? (ln + DKT - 1) / DKT : 0;
     }
     int rank = 0;
     for (int j = 0; j < p.n_req; ++j) {
@@ -73,7 +85,7 @@ __device__ inline Req ranked_request(int b_req, const DecodeArgs &p) {
     return Req{f, __builtin_amdgcn_readlane(sl, f), __builtin_amdgcn_readlane(ln, f)};
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_bf16_kernel(DecodeArgs p) {
     using GM = Geom<D>;
@@ -82,7 +94,8 @@ void decode_bf16_kernel(DecodeArgs p) {
     constexpr int RPI = GM::RPI, IPT = DKT / RPI;    // rows per 1 KB load, loads per tile
     constexpr int NO = DB * 16;                      // accumulator values per lane
     static_assert(kWaves * 2 * TB >= 2 * (NO + 2) * 64 * 4, "merge area must fit");
-    __shared__ __attribute__((aligned(1024))) char smem[kWaves * 2 * TB];
+    // Tile buffers, then (paged) the request's block ids.
+    __shared__ __attribute__((aligned(1024))) char smem[kWaves * 2 * TB + (PAGED ? kDecodeMaxBlocks * 4 : 0)];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -91,27 +104,52 @@ void decode_bf16_kernel(DecodeArgs p) {
     const int g = blockIdx.x % KVH;
     int r, slot, L;
     if (p.ranked) {
-        const Req q = ranked_request(blockIdx.x / KVH, p);
+        const Req q = ranked_request<PAGED>(blockIdx.x / KVH, p);
         r = q.r;
         slot = q.slot;
         L = q.L;
     } else {
         r = blockIdx.x / KVH;
-        slot = p.slot_ids[r];
+        slot = PAGED ? 0 : p.slot_ids[r];
         L = p.cache_lens[r];
     }
-    if (!req_valid(slot, L, p)) {
+    if (!req_valid<PAGED>(slot, L, p)) {
         if (g == 0 && threadIdx.x == 0)
-            atomicOr(p.err, (int32_t)((slot < 0 || slot >= p.n_slots) ? KEV_DEVERR_SLOT : KEV_DEVERR_CACHE_LEN));
+            atomicOr(p.err, (int32_t)((!PAGED && (slot < 0 || slot >= p.n_slots)) ? KEV_DEVERR_SLOT
+                                                                                   : KEV_DEVERR_CACHE_LEN));
         return;
     }
     const int T = (L + DKT - 1) / DKT;
     const int n_mine = wave < T ? (T - 1 - wave) / kWaves + 1 : 0;   // tiles wave, wave+4, ...
 
     uint16_t *pool = static_cast<uint16_t *>(p.pool);
-    const int64_t plane = (int64_t)p.capacity * D;
+    const int64_t plane = (int64_t)p.capacity * D;   // paged: capacity is the block size
     uint16_t *kbase = pool + ((int64_t)slot * 2 * KVH + g) * plane;
     uint16_t *vbase = kbase + (int64_t)KVH * plane;
+    int *tbl = reinterpret_cast<int *>(smem + kWaves * 2 * TB);
+    if constexpr (PAGED) {
+        // The request's block ids 0..(L-1)/B into LDS; an id outside the pool skips the request.
+        const int n_bl = ((L - 1) >> p.block_shift) + 1;
+        const int32_t *bt = p.block_tables + (int64_t)r * p.max_blocks;
+        int bad = 0;
+        for (int j = threadIdx.x; j < n_bl; j += kWaves * 64) {
+            const int b = bt[j];
+            bad |= (b < 0 || b >= p.n_slots) ? 1 : 0;
+            tbl[j] = b;
+        }
+        if (__syncthreads_or(bad)) {
+            if (g == 0 && threadIdx.x == 0) atomicOr(p.err, (int32_t)KEV_DEVERR_BLOCK);
+            return;
+        }
+    }
+    // Element offset of K row `key` of this unit in the pool (its V row is KVH*plane later).
+    auto row_off = [&](int key) -> int64_t {
+        if constexpr (PAGED)
+            return ((int64_t)tbl[key >> p.block_shift] * 2 * KVH + g) * plane +
+                   (int64_t)(key & (p.capacity - 1)) * D;
+        else
+            return ((int64_t)slot * 2 * KVH + g) * plane + (int64_t)key * D;
+    };
     const uint16_t *knew = static_cast<const uint16_t *>(p.k_new) + ((int64_t)r * KVH + g) * D;
     const uint16_t *vnew = static_cast<const uint16_t *>(p.v_new) + ((int64_t)r * KVH + g) * D;
     lds_t *kbuf = (lds_t *)smem + wave * 2 * TB;
@@ -122,7 +160,7 @@ void decode_bf16_kernel(DecodeArgs p) {
     // needs no ordering against any load.
     if ((T - 1) % kWaves == wave && lane < 2 * (D / 8)) {
         const int part = lane % (D / 8);
-        uint16_t *dst = (lane < D / 8 ? kbase : vbase) + (int64_t)(L - 1) * D + part * 8;
+        uint16_t *dst = pool + row_off(L - 1) + (lane < D / 8 ? 0 : (int64_t)KVH * plane) + part * 8;
         const uint16_t *src = (lane < D / 8 ? knew : vnew) + part * 8;
         *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
     }
@@ -146,9 +184,15 @@ void decode_bf16_kernel(DecodeArgs p) {
         for (int i = 0; i < IPT; ++i) {
             const int key = min(k0 + i * RPI + lrow, L - 1);
             const bool nw = key == L - 1;
-            const int64_t off = (int64_t)key * D + lchunk * 8;
-            kr[i] = *reinterpret_cast<const u32x4 *>(nw ? knew + lchunk * 8 : kbase + off);
-            vr[i] = *reinterpret_cast<const u32x4 *>(nw ? vnew + lchunk * 8 : vbase + off);
+            if constexpr (PAGED) {
+                const int64_t off = row_off(key) + lchunk * 8;
+                kr[i] = *reinterpret_cast<const u32x4 *>(nw ? knew + lchunk * 8 : pool + off);
+                vr[i] = *reinterpret_cast<const u32x4 *>(nw ? vnew + lchunk * 8 : pool + off + (int64_t)KVH * plane);
+            } else {
+                const int64_t off = (int64_t)key * D + lchunk * 8;
+                kr[i] = *reinterpret_cast<const u32x4 *>(nw ? knew + lchunk * 8 : kbase + off);
+                vr[i] = *reinterpret_cast<const u32x4 *>(nw ? vnew + lchunk * 8 : vbase + off);
+            }
         }
     };
 
@@ -270,11 +314,13 @@ void decode_bf16_kernel(DecodeArgs p) {
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeArgs &a, int32_t head_dim, hipStream_t s) {
-    const unsigned grid = (unsigned)((int64_t)a.n_req * a.kv_heads);
-    switch (head_dim) {
-    case 64: hipLaunchKernelGGL((decode_bf16_kernel<64>), dim3(grid), dim3(kWaves * 64), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((decode_bf16_kernel<128>), dim3(grid), dim3(kWaves * 64), 0, s, a); break;
+hipError_t launch_decode_bf16(const DecodeArgs &a, int32_t head_dim, bool paged, hipStream_t s) {
+    const dim3 g((unsigned)((int64_t)a.n_req * a.kv_heads)), b(kWaves * 64);
+    switch (head_dim * 2 + (paged ? 1 : 0)) {
+    case 128: hipLaunchKernelGGL((decode_bf16_kernel<64, false>), g, b, 0, s, a); break;
+    case 129: hipLaunchKernelGGL((decode_bf16_kernel<64, true>), g, b, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((decode_bf16_kernel<128, false>), g, b, 0, s, a); break;
+    case 257: hipLaunchKernelGGL((decode_bf16_kernel<128, true>), g, b, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

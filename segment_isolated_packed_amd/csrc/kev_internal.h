@@ -109,16 +109,24 @@ struct PrefillArgs {
     int32_t *err;
 };
 
+// Block ids a paged decode workgroup keeps in LDS: at most this many blocks per request
+// (KEV_PAGED_MAX_BLOCKS of the public header).
+constexpr int kDecodeMaxBlocks = 2048;
+
 struct DecodeArgs {
     const void *q;
     void *pool;
     const int32_t *slot_ids, *cache_lens;
     void *out;
     const void *k_new, *v_new;
-    int32_t n_req, heads, kv_heads, group, n_slots, capacity;
+    int32_t n_req, heads, kv_heads, group;
+    int32_t n_slots, capacity;   // paged: number of blocks, block size
     int32_t ranked;           // 1: workgroups take units longest first (n_req <= 64)
     float scale_log2;
     int32_t *err;
+    // paged pool only: block_tables[n_req][max_blocks], block size 1 << block_shift
+    const int32_t *block_tables;
+    int32_t max_blocks, block_shift;
 };
 
 struct StoreKvArgs {
@@ -137,7 +145,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int64_t g
                                bool prefix, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, int32_t head_dim, int64_t grid,
                               hipStream_t s);
-hipError_t launch_decode_bf16(const DecodeArgs &a, int32_t head_dim, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs &a, int32_t head_dim, bool paged, hipStream_t s);
 hipError_t launch_store_kv(const StoreKvArgs &a, int32_t head_dim, hipStream_t s);
 
 }  // namespace kev

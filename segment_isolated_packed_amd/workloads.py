@@ -361,3 +361,83 @@ def chunked_case(seed: int = 46) -> ChunkedCase:
     return make_chunked([2048] * 8, prefix, 28, 4, 128, capacity=8192, n_slots=12, seed=seed,
                         name="chunked_qwen25_7b")
 
+
+
+@dataclass
+class PagedDecodeCase:
+    """Decode inputs over a paged pool: request r's position p lives in block
+    block_tables[r, p // block_size], row p % block_size."""
+    name: str
+    heads: int
+    kv_heads: int
+    head_dim: int
+    block_size: int
+    seed: int
+    block_tables: np.ndarray  # int32 [n_req, max_blocks]; unused entries -1
+    cache_lens: np.ndarray    # int32 [n_req], positions after the append
+    q: np.ndarray             # [n_req, heads, d]
+    k_new: np.ndarray         # [n_req, kv_heads, d]
+    v_new: np.ndarray
+    pool: np.ndarray          # [n_blocks, 2, kv_heads, block_size, d]
+    dtype: str = BF16
+
+    @property
+    def n_req(self) -> int:
+        return len(self.cache_lens)
+
+    @property
+    def n_blocks(self) -> int:
+        return self.pool.shape[0]
+
+    def blocks_in_use(self) -> int:
+        return int(((self.cache_lens.astype(np.int64) + self.block_size - 1) // self.block_size).sum())
+
+    def algorithmic_bytes(self) -> int:
+        """As for the slot decode, plus the block ids each request reads."""
+        d, hk, hq = self.head_dim, self.kv_heads, self.heads
+        cached = int((self.cache_lens.astype(np.int64) - 1).sum()) * hk * d * 2 * 2
+        return cached + self.n_req * (hk * d * 2 * 2 * 2 + hq * d * 2 * 2) + 4 * self.blocks_in_use()
+
+
+def paged_from_slots(dc: DecodeCase, block_size: int, spare_blocks: int = 0, seed: int = 47) -> PagedDecodeCase:
+    """The same decode step over a paged pool: each request's cached rows are cut into blocks
+    of `block_size` positions (only as many as its length needs, as an on-demand allocator
+    would hand out; a block past the slot's capacity is zero-padded) and scattered over a pool
+    of shuffled blocks, plus `spare_blocks` unused ones.  Decoding it must give the slot decode's output, and the pools after the append
+    hold the same rows."""
+    rng = np.random.default_rng(seed)
+    B = block_size
+    need = (dc.cache_lens.astype(np.int64) + B - 1) // B
+    n_blocks = int(need.sum()) + spare_blocks
+    perm = rng.permutation(n_blocks).astype(np.int32)
+    max_blocks = max(int(need.max()), 1)
+    tables = np.full((dc.n_req, max_blocks), -1, np.int32)
+    pool = np.zeros((n_blocks, 2, dc.kv_heads, B, dc.head_dim), dtype=dc.pool.dtype)
+    if spare_blocks > 0:
+        spare = np.empty((spare_blocks,) + pool.shape[1:], dtype=pool.dtype)
+        _normal_into(rng, spare.reshape(-1, dc.head_dim))
+        pool[perm[n_blocks - spare_blocks:]] = spare
+    nxt = 0
+    for r in range(dc.n_req):
+        s, L = int(dc.slot_ids[r]), int(dc.cache_lens[r])
+        for j in range(int(need[r])):
+            b = int(perm[nxt])
+            nxt += 1
+            tables[r, j] = b
+            rows = dc.pool[s, :, :, j * B:min((j + 1) * B, dc.capacity)]
+            pool[b, :, :, :rows.shape[2]] = rows
+    return PagedDecodeCase(f"{dc.name}_paged{B}", dc.heads, dc.kv_heads, dc.head_dim, B, seed, tables,
+                           dc.cache_lens.copy(), dc.q, dc.k_new, dc.v_new, pool)
+
+
+def slots_from_paged_pool(pc: PagedDecodeCase, pool: np.ndarray, dc: DecodeCase) -> np.ndarray:
+    """Rows 0..L-1 of every request gathered back from a paged pool into dc's slot layout
+    (a copy of dc.pool with those rows replaced)."""
+    out = dc.pool.copy()
+    B = pc.block_size
+    for r in range(pc.n_req):
+        s, L = int(dc.slot_ids[r]), int(pc.cache_lens[r])
+        for j in range((L + B - 1) // B):
+            n = min(B, L - j * B)
+            out[s, :, :, j * B:j * B + n] = pool[pc.block_tables[r, j], :, :, :n]
+    return out

@@ -97,6 +97,28 @@ def test_chunked_prefill_argument_checks(lib):
     assert _chunked(lib, heads=6) == K.KEV_ERR_INVALID_ARG                # heads not a multiple of kv_heads
 
 
+def _paged(lib, n_req=4, heads=32, n_blocks=64, bs=16, kvh=8, d=128, dtype=0, max_blocks=8, null=False):
+    p = ctypes.c_void_p(16)
+    pool = K.PagedPool(16, n_blocks, bs, kvh, d, dtype)
+    return lib.kev_paged_attn_decode(p, None if null else ctypes.byref(pool), p, max_blocks, p, p, p, p,
+                                     n_req, heads, None)
+
+
+def test_paged_decode_argument_checks(lib):
+    # every case fails on the host before any HIP call
+    assert _paged(lib, null=True) == K.KEV_ERR_INVALID_ARG
+    assert _paged(lib, bs=24) == K.KEV_ERR_INVALID_ARG          # block size not a power of two
+    assert _paged(lib, bs=0) == K.KEV_ERR_INVALID_ARG
+    assert _paged(lib, n_blocks=0) == K.KEV_ERR_INVALID_ARG
+    assert _paged(lib, max_blocks=0) == K.KEV_ERR_INVALID_ARG
+    assert _paged(lib, heads=30) == K.KEV_ERR_INVALID_ARG       # not a multiple of kv_heads
+    assert _paged(lib, dtype=1) == K.KEV_ERR_UNSUPPORTED
+    assert _paged(lib, d=96) == K.KEV_ERR_UNSUPPORTED
+    assert _paged(lib, heads=8 * 33) == K.KEV_ERR_UNSUPPORTED   # more than 32 q heads per KV head
+    assert _paged(lib, n_req=0) == K.KEV_OK
+    assert _paged(lib, n_req=-1) == K.KEV_ERR_INVALID_ARG
+
+
 def _decode(lib, n_req=4, heads=32, n_slots=8, cap=64, kvh=8, d=128, dtype=0, null=False):
     pool = K.KvPool(16, n_slots, cap, kvh, d, dtype)
     p = None if null else ctypes.c_void_p(16)
