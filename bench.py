@@ -11,8 +11,9 @@ entries counted: 4 * d * heads * sum L(L+1)/2 FLOPs per call) over the average d
 of the prefill call measured with HIP events on the launch stream.  The decode's
 achieved HBM GB/s (algorithmic bytes over event-timed duration) is reported beside it,
 and so are more calls timed the same way: the prefill that also stores every question's K/V
-into its slot, a chunked prefill of 8 long prompts against their cached prefixes, and the
-decode over a paged (block-table) pool holding the same rows.
+into its slot, a chunked prefill of 8 long prompts against their cached prefixes, the
+decode over a paged (block-table) pool holding the same rows, and the decode of batches cut
+to 1, 4 and 16 requests (low occupancy).
 """
 from __future__ import annotations
 
@@ -235,6 +236,39 @@ def main():
                 "rows_reserved_slots": dc.n_slots * dc.capacity})
             del ppool, pq, pkn, pvn, pout
 
+    # A batch that has shrunk as requests finished: the first n requests of the decode workload
+    # (same pool), with the automatic split of units over workgroups and with splitting off.
+    low_res = []
+    if do_dec:
+        for n in (1, 4, 16):
+            lq, lkn, lvn = dq[:n].contiguous(), dkn[:n].contiguous(), dvn[:n].contiguous()
+            lids, llens = dids[:n].contiguous(), dlens[:n].contiguous()
+            lout = torch.empty_like(lq)
+            L = dc.cache_lens[:n].astype(np.int64)
+            lbytes = int((L - 1).sum()) * dc.kv_heads * dc.head_dim * 2 * 2 + \
+                n * (dc.kv_heads * dc.head_dim * 2 * 2 * 2 + dc.heads * dc.head_dim * 2 * 2)
+            row = {"n_req": n, "algorithmic_mb": lbytes / 1e6, "max_len": int(L.max())}
+            prev = os.environ.pop("KEV_DECODE_SPLITS", None)
+            for mode in ("auto", "unsplit"):
+                if mode == "unsplit":
+                    os.environ["KEV_DECODE_SPLITS"] = "1"
+                lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+                for i in range(max(args.warmup, 1) + args.steps):
+                    torch.sum(flush_rows, dim=1, dtype=torch.int32, out=flush_sink)
+                    e = lev[i - max(args.warmup, 1)] if i >= max(args.warmup, 1) else None
+                    if e: e[0].record(stream)
+                    K.kev_slot_attn_decode(lq, dpool, lids, llens, lkn, lvn, out=lout)
+                    if e: e[1].record(stream)
+                torch.cuda.synchronize()
+                os.environ.pop("KEV_DECODE_SPLITS", None)
+                if prev is not None:
+                    os.environ["KEV_DECODE_SPLITS"] = prev
+                ms = float(np.mean([e[0].elapsed_time(e[1]) for e in lev]))
+                row[mode] = {"us": ms * 1e3, "gbps": lbytes / (ms * 1e-3) / 1e9}
+            low_res.append(row)
+        if K.kev_get_device_errors():
+            raise RuntimeError("device error flags in the low-occupancy decode leg")
+
     # Chunked prefill against slot prefixes (kev_chunked_prefill_slots) on its own workload:
     # 8 long prompts at four different chunk phases, packed into one call.
     chunk_res = None
@@ -323,6 +357,7 @@ def main():
             "call": "kev_packed_attn_prefill_slots: prefill + every question's K/V stored into its slot"},
         "chunked_prefill": chunk_res,
         "paged_decode": paged_res or None,
+        "decode_low_occupancy": low_res or None,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and do_pre:

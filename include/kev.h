@@ -138,6 +138,13 @@ typedef struct {
  * with KEV_ERR_BAD_SLOT under KEV_CHECK=1).  A slot is never truncated or
  * re-laid out: a length past capacity is an error, not a reallocation.
  * head_dim must be 64 or 128 and equal to the pool's.
+ *
+ * Small batches (fewer (request, KV head) units than CUs -- e.g. a batch that
+ * has shrunk as requests finished and left, Kev part 2, gsyq.cn, section 2.3)
+ * split every unit's positions over up to 8 workgroups and merge their
+ * partial softmax states in a second kernel, using the stream's workspace.
+ * The environment variable KEV_DECODE_SPLITS=N (1..32) forces N splits per
+ * unit (1: never split); results agree within rounding either way.
  */
 int kev_slot_attn_decode(const void *q, const kev_kv_pool *kv_pool,
                          const int32_t *slot_ids, const int32_t *cache_lens, void *out,
@@ -187,7 +194,8 @@ typedef struct kev_paged_pool {
  * the call (rejected with KEV_ERR_BAD_SLOT under KEV_CHECK=1; undefined
  * otherwise).  A request with a block id outside the pool, or a length out
  * of range, is skipped (KEV_DEVERR_BLOCK / KEV_DEVERR_CACHE_LEN).  head_dim
- * must be 64 or 128 and at most 32 query heads may share a KV head.
+ * must be 64 or 128 and at most 32 query heads may share a KV head.  Small
+ * batches are split as for kev_slot_attn_decode.
  */
 int kev_paged_attn_decode(const void *q, const kev_paged_pool *kv_pool, const int32_t *block_tables,
                           int32_t max_blocks, const int32_t *cache_lens, void *out,

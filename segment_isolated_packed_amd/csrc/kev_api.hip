@@ -35,6 +35,7 @@ struct State {
     std::mutex mu;
     std::map<int, int32_t *> err_word;                        // device -> error word
     std::map<std::pair<int, void *>, Buffer> sched_ws;        // (device, stream)
+    std::map<std::pair<int, void *>, Buffer> decode_ws;       // (device, stream): split states
 };
 
 State &state() {
@@ -305,6 +306,20 @@ int host_check_paged(const std::vector<int32_t> &tables, const std::vector<int32
     return KEV_OK;
 }
 
+// Workgroups per decode unit (request, KV head).  With fewer units than the CUs hold at once
+// (two workgroups each), one workgroup per unit leaves CUs idle and each unit's time is the
+// latency of a few sequential tile loads, so its tiles are split: about two workgroups per CU
+// in total, at most 8 per unit (more splits cost more in the merge than they save; measured
+// on the 64-request decode workload cut to 1..32 requests).  KEV_DECODE_SPLITS=N forces N.
+int decode_splits(int64_t units, int cus) {
+    if (const char *e = std::getenv("KEV_DECODE_SPLITS")) {
+        const int n = std::atoi(e);
+        if (n >= 1) return std::min(n, kMaxDecodeSplits);
+    }
+    if (units >= (int64_t)cus) return 1;
+    return (int)std::min<int64_t>(8, (2 * (int64_t)cus + units - 1) / units);
+}
+
 // Launch a decode (slot or paged pool) once the pool-specific fields of `da` are set.
 int run_decode(DecodeArgs &da, const void *q, void *data, int32_t kv_heads, int32_t head_dim,
                const int32_t *cache_lens, void *out, const void *k_new, const void *v_new, int32_t n_req,
@@ -324,13 +339,22 @@ int run_decode(DecodeArgs &da, const void *q, void *data, int32_t kv_heads, int3
     da.kv_heads = kv_heads;
     da.group = heads / kv_heads;
     da.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
-    if ((int64_t)n_req * kv_heads > INT32_MAX) return KEV_ERR_INVALID_ARG;
-    // Longest units first when the grid does not fit the CUs at once (two workgroups each);
-    // otherwise every workgroup starts at once and the order does not matter.
+    const int64_t units = (int64_t)n_req * kv_heads;
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         return KEV_ERR_DEVICE;
-    da.ranked = (n_req <= 64 && (int64_t)n_req * kv_heads > 2 * (int64_t)cus) ? 1 : 0;
+    da.n_split = decode_splits(units, cus);
+    if (units * da.n_split > INT32_MAX) return KEV_ERR_INVALID_ARG;
+    if (da.n_split > 1) {
+        void *ws = nullptr;
+        const size_t bytes = (size_t)units * da.n_split * da.group * (head_dim + 2) * sizeof(float);
+        rc = workspace(state().decode_ws, dev, stream, bytes, &ws);
+        if (rc) return rc;
+        da.part = static_cast<float *>(ws);
+    }
+    // Longest units first when the grid does not fit the CUs at once (two workgroups each);
+    // otherwise every workgroup starts at once and the order does not matter.
+    da.ranked = (da.n_split == 1 && n_req <= 64 && units > 2 * (int64_t)cus) ? 1 : 0;
     return to_status(launch_decode_bf16(da, head_dim, paged, stream));
 }
 

@@ -41,6 +41,15 @@
 // rows then B V rows, i.e. it is a slot of capacity B.  The workgroup first
 // copies the request's block ids into LDS (checking them), then every row
 // address of a tile is looked up there; the rest of the kernel is unchanged.
+//
+// Split units (the SPLIT instantiation).  With few requests -- a batch that
+// shrinks as requests finish and leave (Kev part 2, gsyq.cn, section 2.3) --
+// one workgroup per unit leaves most CUs idle and each unit's time is bound
+// by the latency of one workgroup's loads.  The unit's tiles are then cut
+// into n_split contiguous ranges, one workgroup each; a workgroup writes its
+// unnormalised state (O^T, running max, row sum per query head) to a
+// workspace, and decode_merge_kernel combines the ranges with the same
+// rescaling identity and writes the output.
 #include "kev_internal.h"
 #include "kev_mfma_core.h"
 #include "../../include/kev.h"
@@ -85,7 +94,21 @@ __device__ inline Req ranked_request(int b_req, const DecodeArgs &p) {
     return Req{f, __builtin_amdgcn_readlane(sl, f), __builtin_amdgcn_readlane(ln, f)};
 }
 
-template <int D, bool PAGED>
+// A unit with T tiles uses min(T, n_split) splits, so every split it uses has at least one
+// tile; split s < that count takes tiles [split_begin(s), split_begin(s + 1)).
+__device__ inline int splits_used(int T, int S) { return min(T, S); }
+__device__ inline int split_begin(int s, int T, int Se) { return (int)((int64_t)s * T / Se); }
+
+// Paged: the request's block ids 0..(L-1)/B, checked against the pool (all threads agree).
+__device__ inline bool blocks_valid(const DecodeArgs &p, int r, int L) {
+    const int n_bl = ((L - 1) >> p.block_shift) + 1;
+    const int32_t *bt = p.block_tables + (int64_t)r * p.max_blocks;
+    int bad = 0;
+    for (int j = threadIdx.x; j < n_bl; j += blockDim.x) bad |= (bt[j] < 0 || bt[j] >= p.n_slots) ? 1 : 0;
+    return !__syncthreads_or(bad);
+}
+
+template <int D, bool PAGED, bool SPLIT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_bf16_kernel(DecodeArgs p) {
     using GM = Geom<D>;
@@ -101,26 +124,32 @@ void decode_bf16_kernel(DecodeArgs p) {
     const int lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
     const int G = p.group, KVH = p.kv_heads;
-    const int g = blockIdx.x % KVH;
+    const int ublk = SPLIT ? blockIdx.x / p.n_split : blockIdx.x;   // unit = request * KVH + head
+    const int split = SPLIT ? blockIdx.x - ublk * p.n_split : 0;
+    const int g = ublk % KVH;
     int r, slot, L;
-    if (p.ranked) {
+    if (!SPLIT && p.ranked) {
         const Req q = ranked_request<PAGED>(blockIdx.x / KVH, p);
         r = q.r;
         slot = q.slot;
         L = q.L;
     } else {
-        r = blockIdx.x / KVH;
+        r = ublk / KVH;
         slot = PAGED ? 0 : p.slot_ids[r];
         L = p.cache_lens[r];
     }
     if (!req_valid<PAGED>(slot, L, p)) {
-        if (g == 0 && threadIdx.x == 0)
+        if (g == 0 && split == 0 && threadIdx.x == 0)
             atomicOr(p.err, (int32_t)((!PAGED && (slot < 0 || slot >= p.n_slots)) ? KEV_DEVERR_SLOT
                                                                                    : KEV_DEVERR_CACHE_LEN));
         return;
     }
     const int T = (L + DKT - 1) / DKT;
-    const int n_mine = wave < T ? (T - 1 - wave) / kWaves + 1 : 0;   // tiles wave, wave+4, ...
+    const int n_used = SPLIT ? splits_used(T, p.n_split) : 1;
+    if (split >= n_used) return;                                      // a split the unit does not use
+    const int t0 = SPLIT ? split_begin(split, T, n_used) : 0;         // this workgroup's tiles [t0, t1)
+    const int t1 = SPLIT ? split_begin(split + 1, T, n_used) : T;
+    const int n_mine = wave < t1 - t0 ? (t1 - t0 - 1 - wave) / kWaves + 1 : 0;   // t0+wave, +4, ...
 
     uint16_t *pool = static_cast<uint16_t *>(p.pool);
     const int64_t plane = (int64_t)p.capacity * D;   // paged: capacity is the block size
@@ -138,7 +167,7 @@ void decode_bf16_kernel(DecodeArgs p) {
             tbl[j] = b;
         }
         if (__syncthreads_or(bad)) {
-            if (g == 0 && threadIdx.x == 0) atomicOr(p.err, (int32_t)KEV_DEVERR_BLOCK);
+            if (g == 0 && split == 0 && threadIdx.x == 0) atomicOr(p.err, (int32_t)KEV_DEVERR_BLOCK);
             return;
         }
     }
@@ -158,7 +187,7 @@ void decode_bf16_kernel(DecodeArgs p) {
     // In-place append of the new token (by the wavefront that owns the unit's last tile).
     // That tile reads row L-1 from k_new / v_new and no other tile reads it, so the store
     // needs no ordering against any load.
-    if ((T - 1) % kWaves == wave && lane < 2 * (D / 8)) {
+    if (t1 == T && (T - 1 - t0) % kWaves == wave && lane < 2 * (D / 8)) {
         const int part = lane % (D / 8);
         uint16_t *dst = pool + row_off(L - 1) + (lane < D / 8 ? 0 : (int64_t)KVH * plane) + part * 8;
         const uint16_t *src = (lane < D / 8 ? knew : vnew) + part * 8;
@@ -204,9 +233,9 @@ void decode_bf16_kernel(DecodeArgs p) {
     float m_run = -INFINITY, l_run = 0.f;
     const float cs = p.scale_log2;
 
-    if (n_mine > 0) load_tile(wave);
+    if (n_mine > 0) load_tile(t0 + wave);
     for (int it = 0; it < n_mine; ++it) {
-        const int j = wave + it * kWaves;
+        const int j = t0 + wave + it * kWaves;
         // Registers -> this wavefront's LDS tiles.  LDS operations of one wavefront run in
         // order, so these writes land after the previous tile's fragment reads and before
         // this tile's.
@@ -299,6 +328,21 @@ void decode_bf16_kernel(DecodeArgs p) {
     // Lanes l and l+32 hold the same head; rows d = db*32 + 8*(i/4) + 4*half + i%4.
     const float l_tot = sum_halves(l_run);
     if (col >= G) return;
+    if constexpr (SPLIT) {
+        // Unnormalised state of query head col over this tile range: O^T rows, max, row sum.
+        float *po = p.part + ((int64_t)blockIdx.x * G + col) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+                *reinterpret_cast<f32x4 *>(po + db * 32 + g4 * 8 + half * 4) =
+                    f32x4{o[db][g4 * 4], o[db][g4 * 4 + 1], o[db][g4 * 4 + 2], o[db][g4 * 4 + 3]};
+        if (half == 0) {
+            float *pml = p.part + (int64_t)gridDim.x * G * D + ((int64_t)blockIdx.x * G + col) * 2;
+            *reinterpret_cast<float2 *>(pml) = float2{m_run, l_tot};
+        }
+        return;
+    }
     const float inv = 1.f / l_tot;
     uint16_t *op = static_cast<uint16_t *>(p.out) + ((int64_t)r * p.heads + g * G + col) * D;
 #pragma unroll
@@ -312,18 +356,87 @@ void decode_bf16_kernel(DecodeArgs p) {
         }
 }
 
+// Combines the partial states of every unit (one workgroup per unit): with M the largest
+// running max over the unit's splits, out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// The weights are formed once per head in LDS; then each thread issues the loads of all
+// splits of its output element before summing, so the reads overlap.  Units of invalid
+// requests are skipped (the split kernel flagged them), so their outputs stay untouched.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs p) {
+    __shared__ float wts[kMaxDecodeSplits * 32];   // [split][head]: m, then the weight
+    __shared__ float sums[kMaxDecodeSplits * 32];  // [split][head]: l
+    const int u = blockIdx.x, KVH = p.kv_heads, G = p.group, S = p.n_split;
+    const int r = u / KVH, g = u % KVH;
+    const int slot = PAGED ? 0 : p.slot_ids[r];
+    const int L = p.cache_lens[r];
+    if (!req_valid<PAGED>(slot, L, p)) return;
+    if constexpr (PAGED) {
+        if (!blocks_valid(p, r, L)) return;
+    }
+    const int Se = splits_used((L + DKT - 1) / DKT, S);
+    const int64_t n_part = (int64_t)gridDim.x * S;   // workgroups of the split kernel
+    const float *po = p.part + (int64_t)u * S * G * D;
+    const float2 *pml = reinterpret_cast<const float2 *>(p.part + n_part * G * D) + (int64_t)u * S * G;
+    for (int e = threadIdx.x; e < Se * G; e += blockDim.x) {
+        const float2 ml = pml[e];
+        wts[e] = ml.x;
+        sums[e] = ml.y;
+    }
+    __syncthreads();
+    if (threadIdx.x < G) {
+        const int h = threadIdx.x;
+        float mx = -INFINITY;
+        for (int s = 0; s < Se; ++s) mx = fmaxf(mx, wts[s * G + h]);
+        float l = 0.f;
+        for (int s = 0; s < Se; ++s) {
+            const float w = __builtin_amdgcn_exp2f(wts[s * G + h] - mx);
+            wts[s * G + h] = w;
+            l += w * sums[s * G + h];
+        }
+        const float inv = 1.f / l;
+        for (int s = 0; s < Se; ++s) wts[s * G + h] *= inv;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < G * (D / 4); e += blockDim.x) {
+        const int h = e / (D / 4), d4 = e % (D / 4);
+        f32x4 v[kMaxDecodeSplits];
+#pragma unroll
+        for (int s = 0; s < kMaxDecodeSplits; ++s)
+            if (s < Se) v[s] = *reinterpret_cast<const f32x4 *>(po + ((int64_t)s * G + h) * D + d4 * 4);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kMaxDecodeSplits; ++s)
+            if (s < Se) acc += wts[s * G + h] * v[s];
+        *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(p.out) + ((int64_t)r * p.heads + g * G + h) * D + d4 * 4) =
+            __builtin_convertvector(acc, bf16x4);
+    }
+}
+
 }  // namespace
 
+template <int D, bool PAGED>
+hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t s) {
+    const int64_t units = (int64_t)a.n_req * a.kv_heads;
+    const dim3 b(kWaves * 64);
+    if (a.n_split <= 1) {
+        hipLaunchKernelGGL((decode_bf16_kernel<D, PAGED, false>), dim3((unsigned)units), b, 0, s, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((decode_bf16_kernel<D, PAGED, true>), dim3((unsigned)(units * a.n_split)), b, 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_merge_kernel<D, PAGED>), dim3((unsigned)units), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode_bf16(const DecodeArgs &a, int32_t head_dim, bool paged, hipStream_t s) {
-    const dim3 g((unsigned)((int64_t)a.n_req * a.kv_heads)), b(kWaves * 64);
     switch (head_dim * 2 + (paged ? 1 : 0)) {
-    case 128: hipLaunchKernelGGL((decode_bf16_kernel<64, false>), g, b, 0, s, a); break;
-    case 129: hipLaunchKernelGGL((decode_bf16_kernel<64, true>), g, b, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((decode_bf16_kernel<128, false>), g, b, 0, s, a); break;
-    case 257: hipLaunchKernelGGL((decode_bf16_kernel<128, true>), g, b, 0, s, a); break;
+    case 128: return launch_decode_d<64, false>(a, s);
+    case 129: return launch_decode_d<64, true>(a, s);
+    case 256: return launch_decode_d<128, false>(a, s);
+    case 257: return launch_decode_d<128, true>(a, s);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace kev

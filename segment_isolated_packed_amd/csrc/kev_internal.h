@@ -112,6 +112,8 @@ struct PrefillArgs {
 // Block ids a paged decode workgroup keeps in LDS: at most this many blocks per request
 // (KEV_PAGED_MAX_BLOCKS of the public header).
 constexpr int kDecodeMaxBlocks = 2048;
+// Most workgroups one decode unit (request, KV head) is split over.
+constexpr int kMaxDecodeSplits = 32;
 
 struct DecodeArgs {
     const void *q;
@@ -127,6 +129,10 @@ struct DecodeArgs {
     // paged pool only: block_tables[n_req][max_blocks], block size 1 << block_shift
     const int32_t *block_tables;
     int32_t max_blocks, block_shift;
+    // n_split > 1: each unit's tiles are cut into n_split ranges whose unnormalised states go
+    // to part (o: [units * n_split][group][head_dim] fp32, then {max, sum} per head)
+    int32_t n_split;
+    float *part;
 };
 
 struct StoreKvArgs {

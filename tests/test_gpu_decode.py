@@ -6,7 +6,7 @@ import torch
 import oracle
 import segment_isolated_packed_amd as K
 from segment_isolated_packed_amd import workloads as W
-from gpu_util import (assert_parity, decode_dev, prefill_dev, say, to_dev_i32, to_host_bits,
+from gpu_util import (assert_parity, decode_dev, prefill_dev, say, to_dev, to_dev_i32, to_host_bits,
                       to_host_f64)
 
 pytestmark = pytest.mark.gpu
@@ -148,3 +148,53 @@ def test_invalid_slot_and_length_are_flagged_and_skipped(monkeypatch):
         with pytest.raises(K.KevError) as e:
             K.kev_slot_attn_decode(**{**t, "slot_ids": to_dev_i32(ids), "cache_lens": to_dev_i32(lens)})
         assert e.value.code == code
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 32])
+@pytest.mark.parametrize("paged", [False, True])
+def test_split_units_match_oracle(orc, monkeypatch, splits, paged):
+    """Each unit's tiles cut over `splits` workgroups (more splits than tiles for the short
+    requests) and merged: the oracle's values and the same appended rows."""
+    lens = [1, 31, 32, 33, 100, 2458]
+    dc = W.make_decode(n_req=len(lens), n_slots=8, capacity=2458, seed=70 + splits, cache_lens=lens)
+    monkeypatch.setenv("KEV_DECODE_SPLITS", str(splits))
+    say(f"decode split={splits} paged={paged} lens={lens}")
+    ref, ref_pool = orc.decode_case(dc, want_pool=True)
+    if paged:
+        pc = W.paged_from_slots(dc, 16, spare_blocks=4)
+        t = dict(q=to_dev(pc.q, W.BF16), kv_pool=to_dev(pc.pool, W.BF16), block_tables=to_dev_i32(pc.block_tables),
+                 cache_lens=to_dev_i32(pc.cache_lens), k_new=to_dev(pc.k_new, W.BF16), v_new=to_dev(pc.v_new, W.BF16))
+        out = K.kev_paged_attn_decode(**t)
+        torch.cuda.synchronize()
+        assert K.kev_get_device_errors() == 0
+        back = W.slots_from_paged_pool(pc, to_host_bits(t["kv_pool"]), dc)
+        for r in range(dc.n_req):
+            s, L = int(dc.slot_ids[r]), int(dc.cache_lens[r])
+            assert np.array_equal(back[s, :, :, :L], ref_pool[s, :, :, :L])
+    else:
+        out, pool = run(dc)
+        assert K.kev_get_device_errors() == 0
+        assert np.array_equal(to_host_bits(pool), ref_pool)
+    assert_parity(to_host_f64(out), ref, dc.dtype, f"decode split={splits} paged={paged}")
+
+
+@pytest.mark.parametrize("n_req", [1, 2, 5])
+def test_low_occupancy_batches(orc, n_req):
+    """A batch that has shrunk to a few requests (automatic split count)."""
+    dc = W.make_decode(n_req=n_req, n_slots=8, seed=80 + n_req)
+    say(f"decode low occupancy n_req={n_req} lens={list(dc.cache_lens)}")
+    out, pool = run(dc)
+    assert K.kev_get_device_errors() == 0
+    ref, ref_pool = orc.decode_case(dc, want_pool=True)
+    assert_parity(to_host_f64(out), ref, dc.dtype, f"decode n_req={n_req}")
+    assert np.array_equal(to_host_bits(pool), ref_pool)
+
+
+def test_full_config_split_and_unsplit_agree(orc, full_case, monkeypatch):
+    ref = orc.decode_case(full_case)
+    for splits in (1, 4):
+        monkeypatch.setenv("KEV_DECODE_SPLITS", str(splits))
+        say(f"decode full config split={splits}")
+        out, _ = run(full_case)
+        assert K.kev_get_device_errors() == 0
+        assert_parity(to_host_f64(out), ref, full_case.dtype, f"decode full config split={splits}")
