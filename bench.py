@@ -91,6 +91,9 @@ def main():
     ap.add_argument("--workload", default="qwen25_7b",
                     choices=["qwen25_7b", "qwen3_8b", "skewed_long"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-legs", action="store_true",
+                    help="time only the prefill and decode calls of the step (profiling runs whose "
+                         "per-kernel averages must not mix in the other legs' launches)")
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
                     help="how the 256 MB MALL is evicted before each decode: read a 512 MiB "
                          "buffer (default), write it, or not at all")
@@ -183,7 +186,8 @@ def main():
     # Prefill-to-slot handoff (kev_packed_attn_prefill_slots) on the same workload: every
     # question's K/V rows stored into its own slot of a pool sized for its longest question.
     slots_res = None
-    if do_pre and pc.dtype == W.BF16:
+    extra = not args.no_extra_legs
+    if extra and do_pre and pc.dtype == W.BF16:
         cap = int(max(pc.seqlens.max(), 1))
         spool = torch.zeros((pc.n_seg + 4, 2, pc.kv_heads, cap, pc.head_dim), dtype=torch.bfloat16, device=dev)
         sids = torch.arange(pc.n_seg, dtype=torch.int32, device=dev)
@@ -206,7 +210,7 @@ def main():
     # The decode over a paged pool (kev_paged_attn_decode): the same requests and rows cut into
     # blocks of B positions scattered over a pool of only the blocks the lengths need.
     paged_res = []
-    if do_dec:
+    if extra and do_dec:
         for B in (16, 64):
             log(f"paged decode, block size {B}")
             pg = W.paged_from_slots(dc, B)
@@ -239,7 +243,7 @@ def main():
     # A batch that has shrunk as requests finished: the first n requests of the decode workload
     # (same pool), with the automatic split of units over workgroups and with splitting off.
     low_res = []
-    if do_dec:
+    if extra and do_dec:
         for n in (1, 4, 16):
             lq, lkn, lvn = dq[:n].contiguous(), dkn[:n].contiguous(), dvn[:n].contiguous()
             lids, llens = dids[:n].contiguous(), dlens[:n].contiguous()
@@ -272,7 +276,7 @@ def main():
     # Chunked prefill against slot prefixes (kev_chunked_prefill_slots) on its own workload:
     # 8 long prompts at four different chunk phases, packed into one call.
     chunk_res = None
-    if args.only in (None, "chunked"):
+    if (extra and args.only is None) or args.only == "chunked":
         log("generating chunked-prefill inputs")
         cc = W.chunked_case()
         cq, ck, cv, cpool = (to_dev(x, W.BF16) for x in (cc.q, cc.k, cc.v, cc.pool))
@@ -295,6 +299,7 @@ def main():
             "ms": c_ms, "effective_tflops": c_tf, "pct_peak": c_tf / PEAK_BF16_TFLOPS * 100,
             "effective_gflop": cc.effective_flops() / 1e9, "algorithmic_mb": cc.algorithmic_bytes() / 1e6,
             "workload": W.CHUNKED_DESCRIPTION, "seed": cc.seed,
+            "kernel_hbm_bytes_per_launch": traffic_for("prefill_bf16_kernel_prefix", source_hash(PREFILL_SOURCES)),
             "call": "kev_chunked_prefill_slots: scheduler + prefill_bf16_kernel<128, prefix> + K/V append"}
         del cq, ck, cv, cpool, cout
 

@@ -358,9 +358,11 @@ void decode_bf16_kernel(DecodeArgs p) {
 
 // Combines the partial states of every unit (one workgroup per unit): with M the largest
 // running max over the unit's splits, out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// The weights are formed once per head in LDS; then each thread issues the loads of all
-// splits of its output element before summing, so the reads overlap.  Units of invalid
-// requests are skipped (the split kernel flagged them), so their outputs stay untouched.
+// Latency decides this kernel's time, so every read is issued at once: the request's length,
+// the {max, sum} pairs and the O rows of all n_split splits (those past the splits the unit
+// used hold stale values that are never combined).  The weights are then formed once per
+// head in LDS.  Units of invalid requests are skipped (the split kernel flagged them), so
+// their outputs stay untouched.
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs p) {
     __shared__ float wts[kMaxDecodeSplits * 32];   // [split][head]: m, then the weight
@@ -369,19 +371,27 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs p) {
     const int r = u / KVH, g = u % KVH;
     const int slot = PAGED ? 0 : p.slot_ids[r];
     const int L = p.cache_lens[r];
+    const int64_t n_part = (int64_t)gridDim.x * S;   // workgroups of the split kernel
+    const float *po = p.part + (int64_t)u * S * G * D;
+    const float2 *pml = reinterpret_cast<const float2 *>(p.part + n_part * G * D) + (int64_t)u * S * G;
+    for (int e = threadIdx.x; e < S * G; e += blockDim.x) {
+        const float2 ml = pml[e];
+        wts[e] = ml.x;
+        sums[e] = ml.y;
+    }
+    constexpr int E4 = D / 4;                  // float4 columns per head
+    const int n_el = G * E4;
+    const bool mine = threadIdx.x < n_el;      // first output element of this thread
+    const int h0 = mine ? threadIdx.x / E4 : 0, d40 = threadIdx.x % E4;
+    f32x4 v[kMaxDecodeSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxDecodeSplits; ++s)
+        if (s < S && mine) v[s] = *reinterpret_cast<const f32x4 *>(po + ((int64_t)s * G + h0) * D + d40 * 4);
     if (!req_valid<PAGED>(slot, L, p)) return;
     if constexpr (PAGED) {
         if (!blocks_valid(p, r, L)) return;
     }
     const int Se = splits_used((L + DKT - 1) / DKT, S);
-    const int64_t n_part = (int64_t)gridDim.x * S;   // workgroups of the split kernel
-    const float *po = p.part + (int64_t)u * S * G * D;
-    const float2 *pml = reinterpret_cast<const float2 *>(p.part + n_part * G * D) + (int64_t)u * S * G;
-    for (int e = threadIdx.x; e < Se * G; e += blockDim.x) {
-        const float2 ml = pml[e];
-        wts[e] = ml.x;
-        sums[e] = ml.y;
-    }
     __syncthreads();
     if (threadIdx.x < G) {
         const int h = threadIdx.x;
@@ -397,18 +407,21 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs p) {
         for (int s = 0; s < Se; ++s) wts[s * G + h] *= inv;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < G * (D / 4); e += blockDim.x) {
-        const int h = e / (D / 4), d4 = e % (D / 4);
-        f32x4 v[kMaxDecodeSplits];
-#pragma unroll
-        for (int s = 0; s < kMaxDecodeSplits; ++s)
-            if (s < Se) v[s] = *reinterpret_cast<const f32x4 *>(po + ((int64_t)s * G + h) * D + d4 * 4);
+    uint16_t *out = static_cast<uint16_t *>(p.out) + ((int64_t)r * p.heads + g * G) * D;
+    if (mine) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < kMaxDecodeSplits; ++s)
-            if (s < Se) acc += wts[s * G + h] * v[s];
-        *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(p.out) + ((int64_t)r * p.heads + g * G + h) * D + d4 * 4) =
-            __builtin_convertvector(acc, bf16x4);
+            if (s < Se) acc += wts[s * G + h0] * v[s];
+        *reinterpret_cast<bf16x4 *>(out + h0 * D + d40 * 4) = __builtin_convertvector(acc, bf16x4);
+    }
+    // more than 256 output elements (G * D / 4 > 256): the rest, one split after another
+    for (int e = threadIdx.x + blockDim.x; e < n_el; e += blockDim.x) {
+        const int h = e / E4, d4 = e % E4;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < Se; ++s)
+            acc += wts[s * G + h] * *reinterpret_cast<const f32x4 *>(po + ((int64_t)s * G + h) * D + d4 * 4);
+        *reinterpret_cast<bf16x4 *>(out + h * D + d4 * 4) = __builtin_convertvector(acc, bf16x4);
     }
 }
 
