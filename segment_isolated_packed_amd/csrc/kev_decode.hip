@@ -124,8 +124,10 @@ void decode_bf16_kernel(DecodeArgs p) {
     const int lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
     const int G = p.group, KVH = p.kv_heads;
-    const int ublk = SPLIT ? blockIdx.x / p.n_split : blockIdx.x;   // unit = request * KVH + head
-    const int split = SPLIT ? blockIdx.x - ublk * p.n_split : 0;
+    // Split grids are split-major: the first range of every unit, then the second, ...
+    const int n_units = p.n_req * KVH;
+    const int split = SPLIT ? blockIdx.x / n_units : 0;
+    const int ublk = SPLIT ? blockIdx.x - split * n_units : blockIdx.x;   // unit = request * KVH + head
     const int g = ublk % KVH;
     int r, slot, L;
     if (!SPLIT && p.ranked) {
@@ -330,7 +332,8 @@ void decode_bf16_kernel(DecodeArgs p) {
     if (col >= G) return;
     if constexpr (SPLIT) {
         // Unnormalised state of query head col over this tile range: O^T rows, max, row sum.
-        float *po = p.part + ((int64_t)blockIdx.x * G + col) * D;
+        const int64_t pidx = (int64_t)ublk * p.n_split + split;   // unit-major in the workspace
+        float *po = p.part + (pidx * G + col) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -338,7 +341,7 @@ void decode_bf16_kernel(DecodeArgs p) {
                 *reinterpret_cast<f32x4 *>(po + db * 32 + g4 * 8 + half * 4) =
                     f32x4{o[db][g4 * 4], o[db][g4 * 4 + 1], o[db][g4 * 4 + 2], o[db][g4 * 4 + 3]};
         if (half == 0) {
-            float *pml = p.part + (int64_t)gridDim.x * G * D + ((int64_t)blockIdx.x * G + col) * 2;
+            float *pml = p.part + (int64_t)gridDim.x * G * D + (pidx * G + col) * 2;
             *reinterpret_cast<float2 *>(pml) = float2{m_run, l_tot};
         }
         return;
