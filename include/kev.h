@@ -261,6 +261,17 @@ int kev_chunked_prefill_slots(const void *q, const void *k, const void *v,
                               const kev_kv_pool *kv_pool, const int32_t *slot_ids,
                               const int32_t *prefix_lens, void *stream);
 
+/*
+ * Profiling hook.  Until called again with NULL, every call on this host
+ * thread records `start` (a hipEvent_t passed as void*) on its stream right
+ * before launching its main kernel -- the attention kernel of a prefill (not
+ * the work-list pass or the K/V store), the decode kernel (and, for split
+ * units, its merge kernel) -- and `end` right after it, so the events time
+ * that kernel alone.  Both NULL clears; exactly one NULL is KEV_ERR_INVALID_ARG.
+ * The events are the caller's and must stay valid while set.
+ */
+int kev_set_kernel_events(void *start, void *end);
+
 /* Human-readable text for a kev_status value (static storage). */
 const char *kev_status_string(int status);
 

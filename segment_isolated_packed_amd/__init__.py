@@ -72,12 +72,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kev_status_string.argtypes = [ctypes.c_int]
     L.kev_status_string.restype = ctypes.c_char_p
     L.kev_get_device_errors.argtypes = [P, ctypes.POINTER(I)]
+    L.kev_set_kernel_events.argtypes = [P, P]
     L.kev_prefill_block_rows.argtypes = [I, I, I, I]
     L.kev_prefill_order.argtypes = [I, I, I]
     L.kev_schedule_host.argtypes = [P, I, I, I, P, I, ctypes.POINTER(I)]
     L.kev_schedule_device.argtypes = [P, I, I, I, I, P, I, ctypes.POINTER(I), P]
     for f in (L.kev_packed_attn_prefill, L.kev_slot_attn_decode, L.kev_packed_attn_prefill_slots,
               L.kev_chunked_prefill_slots, L.kev_paged_attn_decode, L.kev_get_device_errors,
+              L.kev_set_kernel_events,
               L.kev_prefill_block_rows, L.kev_prefill_order, L.kev_schedule_host,
               L.kev_schedule_device):
         f.restype = ctypes.c_int
@@ -274,6 +276,14 @@ def kev_chunked_prefill_slots(q, k, v, cu_seqlens, kv_pool, slot_ids, prefix_len
     """
     return _slot_prefill("kev_chunked_prefill_slots", q, k, v, cu_seqlens, kv_pool, slot_ids, prefix_lens,
                          out, total_tokens, stream)
+
+
+def kev_set_kernel_events(start=None, end=None):
+    """Time the main kernel of the following calls on this thread: `start` / `end` are
+    torch.cuda.Event objects (recorded once already, so that they exist) or None to clear."""
+    L = load_library()
+    ptr = lambda e: None if e is None else ctypes.c_void_p(e.cuda_event)
+    _check(L.kev_set_kernel_events(ptr(start), ptr(end)), "kev_set_kernel_events")
 
 
 def kev_get_device_errors(stream=None) -> int:

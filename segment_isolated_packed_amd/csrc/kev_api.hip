@@ -43,6 +43,19 @@ State &state() {
     return *s;
 }
 
+// Events the calls of this host thread record around their main kernel (kev_set_kernel_events).
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_end = nullptr;
+
+// Launch `f` (returning hipError_t) between the optional timing events.
+template <typename F>
+int timed_launch(hipStream_t stream, F f) {
+    if (t_ev_start && hipEventRecord(t_ev_start, stream) != hipSuccess) return KEV_ERR_DEVICE;
+    const hipError_t e = f();
+    if (e != hipSuccess) return KEV_ERR_DEVICE;
+    if (t_ev_end && hipEventRecord(t_ev_end, stream) != hipSuccess) return KEV_ERR_DEVICE;
+    return KEV_OK;
+}
+
 bool check_enabled() {
     const char *e = std::getenv("KEV_CHECK");
     return e && e[0] == '1';
@@ -213,7 +226,7 @@ int prefill_impl(const void *q, const void *k, const void *v, const int32_t *cu_
             pa.n_slots = pre->pool->n_slots;
             pa.capacity = pre->pool->capacity;
         }
-        return to_status(launch_prefill_bf16(pa, head_dim, grid, pre != nullptr, stream));
+        return timed_launch(stream, [&] { return launch_prefill_bf16(pa, head_dim, grid, pre != nullptr, stream); });
     }
     if (pre) return KEV_ERR_UNSUPPORTED;
     pa.heads_per_wg = 1;
@@ -222,7 +235,7 @@ int prefill_impl(const void *q, const void *k, const void *v, const int32_t *cu_
     pa.n_hgroups = heads;
     const int64_t grid = n_max * heads;
     if (grid > INT32_MAX) return KEV_ERR_INVALID_ARG;
-    return to_status(launch_prefill_f32(pa, head_dim, grid, stream));
+    return timed_launch(stream, [&] { return launch_prefill_f32(pa, head_dim, grid, stream); });
 }
 
 // Arguments shared by the two slot-writing prefills: a bf16 pool that matches the K/V heads.
@@ -355,7 +368,7 @@ int run_decode(DecodeArgs &da, const void *q, void *data, int32_t kv_heads, int3
     // Longest units first when the grid does not fit the CUs at once (two workgroups each);
     // otherwise every workgroup starts at once and the order does not matter.
     da.ranked = (da.n_split == 1 && n_req <= 64 && units > 2 * (int64_t)cus) ? 1 : 0;
-    return to_status(launch_decode_bf16(da, head_dim, paged, stream));
+    return timed_launch(stream, [&] { return launch_decode_bf16(da, head_dim, paged, stream); });
 }
 
 }  // namespace
@@ -495,6 +508,13 @@ int kev_paged_attn_decode(const void *q, const kev_paged_pool *pool, const int32
     da.block_shift = __builtin_ctz((unsigned)bs);
     return run_decode(da, q, pool->data, pool->kv_heads, pool->head_dim, cache_lens, out, k_new, v_new, n_req,
                       heads, true, stream);
+}
+
+int kev_set_kernel_events(void *start, void *end) {
+    if ((start == nullptr) != (end == nullptr)) return KEV_ERR_INVALID_ARG;
+    t_ev_start = static_cast<hipEvent_t>(start);
+    t_ev_end = static_cast<hipEvent_t>(end);
+    return KEV_OK;
 }
 
 int kev_get_device_errors(void *stream_, int32_t *flags_out) {

@@ -219,3 +219,10 @@ def test_skewed_long_visits_a_small_fraction_of_global_causal_tiles():
     n = T // 64
     global_causal = n * (n + 1) // 2
     assert tiles / global_causal < 0.04
+
+
+def test_kernel_events_hook_arguments(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.kev_set_kernel_events(p, None) == K.KEV_ERR_INVALID_ARG
+    assert lib.kev_set_kernel_events(None, p) == K.KEV_ERR_INVALID_ARG
+    assert lib.kev_set_kernel_events(None, None) == K.KEV_OK
