@@ -283,6 +283,41 @@ def main():
         if K.kev_get_device_errors():
             raise RuntimeError("device error flags in the low-occupancy decode leg")
 
+    # The other prefill configurations (parity-test cases; reported for context, not `value`).
+    other_res = {}
+    if extra and do_pre:
+        for name in ("qwen3_8b", "skewed_long"):
+            if name == args.workload:
+                continue
+            log(f"prefill {name}")
+            oc = W.prefill_case(name)
+            oq, ok_, ov = (to_dev(x, oc.dtype) for x in (oc.q, oc.k, oc.v))
+            ocu = torch.from_numpy(oc.cu_seqlens).to(dev)
+            oout = torch.empty_like(oq)
+            for _ in range(2):
+                K.kev_packed_attn_prefill(oq, ok_, ov, ocu, out=oout)
+            oev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(10)]
+            for evs in oev:
+                for e in evs:
+                    e.record(stream)
+            torch.cuda.synchronize()
+            for e in oev:
+                e[0].record(stream)
+                K.kev_set_kernel_events(e[2], e[3])
+                K.kev_packed_attn_prefill(oq, ok_, ov, ocu, out=oout)
+                K.kev_set_kernel_events(None, None)
+                e[1].record(stream)
+            torch.cuda.synchronize()
+            if K.kev_get_device_errors():
+                raise RuntimeError(f"device error flags in the {name} prefill leg")
+            cms = float(np.mean([e[0].elapsed_time(e[1]) for e in oev]))
+            kms = float(np.mean([e[2].elapsed_time(e[3]) for e in oev]))
+            other_res[name] = {"tokens": oc.total_tokens, "effective_gflop": oc.effective_flops() / 1e9,
+                               "call_ms": cms, "call_tflops": oc.effective_flops() / (cms * 1e-3) / 1e12,
+                               "kernel_ms": kms, "kernel_tflops": oc.effective_flops() / (kms * 1e-3) / 1e12,
+                               "workload": W.PREFILL_DESCRIPTIONS[name]}
+            del oq, ok_, ov, oout
+
     # Chunked prefill against slot prefixes (kev_chunked_prefill_slots) on its own workload:
     # 8 long prompts at four different chunk phases, packed into one call.
     chunk_res = None
@@ -376,6 +411,7 @@ def main():
             "store_bytes": slots_res["store_bytes"], "slot_capacity": slots_res["slot_capacity"],
             "store_gbps_incl_launch": slots_res["store_bytes"] / max(slots_res["ms"] - pre_avg, 1e-6) / 1e6,
             "call": "kev_packed_attn_prefill_slots: prefill + every question's K/V stored into its slot"},
+        "prefill_other_configs": other_res or None,
         "chunked_prefill": chunk_res,
         "paged_decode": paged_res or None,
         "decode_low_occupancy": low_res or None,
