@@ -172,6 +172,7 @@ int prefill_impl(const void *q, const void *k, const void *v, const int32_t *cu_
     if (heads % kv_heads != 0) return KEV_ERR_INVALID_ARG;
     if (dtype != KEV_BF16 && dtype != KEV_F32) return KEV_ERR_UNSUPPORTED;
     if (!prefill_supported(head_dim, dtype)) return KEV_ERR_UNSUPPORTED;
+    if (pre && dtype != KEV_BF16) return KEV_ERR_UNSUPPORTED;   // slot prefixes: bf16 pools only
     if (n_seg == 0) return total_tokens == 0 ? KEV_OK : KEV_ERR_BAD_SEQLENS;
     if (!cu_seqlens) return KEV_ERR_INVALID_ARG;
     if (total_tokens > 0 && (!q || !k || !v || !out)) return KEV_ERR_INVALID_ARG;
@@ -228,7 +229,6 @@ int prefill_impl(const void *q, const void *k, const void *v, const int32_t *cu_
         }
         return timed_launch(stream, [&] { return launch_prefill_bf16(pa, head_dim, grid, pre != nullptr, stream); });
     }
-    if (pre) return KEV_ERR_UNSUPPORTED;
     pa.heads_per_wg = 1;
     pa.row_blocks = 1;
     pa.block_rows = kF32BlockRows;
