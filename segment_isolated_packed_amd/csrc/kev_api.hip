@@ -365,9 +365,16 @@ int run_decode(DecodeArgs &da, const void *q, void *data, int32_t kv_heads, int3
         if (rc) return rc;
         da.part = static_cast<float *>(ws);
     }
-    // Longest units first when the grid does not fit the CUs at once (two workgroups each);
-    // otherwise every workgroup starts at once and the order does not matter.
-    da.ranked = (da.n_split == 1 && n_req <= 64 && units > 2 * (int64_t)cus) ? 1 : 0;
+    // Unit order (requests ranked by length inside the kernel, at most 64 requests): longest
+    // first when the grid does not fit the CUs at once (two workgroups each); when it fits but
+    // some CUs hold two workgroups, a long and a short unit share each such CU (measured on the
+    // 64-request decode workload: 61.4 us against 67.7 us in request order).
+    da.ranked = 0;
+    da.cus = cus;
+    if (da.n_split == 1 && n_req <= 64) {
+        if (units > 2 * (int64_t)cus) da.ranked = 1;
+        else if (units > cus) da.ranked = 2;
+    }
     return timed_launch(stream, [&] { return launch_decode_bf16(da, head_dim, paged, stream); });
 }
 

@@ -31,7 +31,8 @@
 //     no global partials;
 //   - when there are more units than the CUs hold at once (and at most 64
 //     requests), workgroups are issued longest unit first, so the short units
-//     fill in at the end.
+//     fill in at the end; when every unit is resident at once but CUs hold two,
+//     long and short units are paired on a CU, so no CU is left with two long ones.
 //
 // Paged variant (the PAGED instantiation).  The cache may instead be cut into
 // fixed-size blocks of B positions placed anywhere in the pool, request r
@@ -127,11 +128,18 @@ void decode_bf16_kernel(DecodeArgs p) {
     // Split grids are split-major: the first range of every unit, then the second, ...
     const int n_units = p.n_req * KVH;
     const int split = SPLIT ? blockIdx.x / n_units : 0;
-    const int ublk = SPLIT ? blockIdx.x - split * n_units : blockIdx.x;   // unit = request * KVH + head
+    int ublk = SPLIT ? blockIdx.x - split * n_units : blockIdx.x;   // unit = request * KVH + head
+    if (!SPLIT && p.ranked == 2) {
+        // Paired order: the dispatcher gives every CU one workgroup of the first `cus` and then
+        // a second one, so workgroups b and b + cus share a CU.  Units are ranked longest first
+        // and workgroup b + cus takes the unit ranked as far from the end as b is from the
+        // start: each CU holding two units gets a long one and a short one.
+        ublk = blockIdx.x < p.cus ? blockIdx.x : n_units - 1 - (blockIdx.x - p.cus);
+    }
     const int g = ublk % KVH;
     int r, slot, L;
     if (!SPLIT && p.ranked) {
-        const Req q = ranked_request<PAGED>(blockIdx.x / KVH, p);
+        const Req q = ranked_request<PAGED>(ublk / KVH, p);
         r = q.r;
         slot = q.slot;
         L = q.L;

@@ -123,7 +123,8 @@ struct DecodeArgs {
     const void *k_new, *v_new;
     int32_t n_req, heads, kv_heads, group;
     int32_t n_slots, capacity;   // paged: number of blocks, block size
-    int32_t ranked;           // 1: workgroups take units longest first (n_req <= 64)
+    int32_t ranked;           // 1: units longest first; 2: long and short units paired per CU (n_req <= 64)
+    int32_t cus;              // compute units of the device (paired order)
     float scale_log2;
     int32_t *err;
     // paged pool only: block_tables[n_req][max_blocks], block size 1 << block_shift
