@@ -200,6 +200,18 @@ def main():
             K.kev_packed_attn_prefill(q, k, v, cu, out=out)
             K.kev_set_kernel_events(None, None)
         torch.cuda.synchronize()
+        # Back-to-back calls (one event pair around 100 launches, 5 repeats, median): the
+        # throughput a caller issuing prefills one after another sees.
+        b2b = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(100):
+                K.kev_packed_attn_prefill(q, k, v, cu, out=out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            b2b.append(e0.elapsed_time(e1) / 100)
+        pre_b2b_ms = float(np.median(b2b))
 
     # Prefill-to-slot handoff (kev_packed_attn_prefill_slots) on the same workload: every
     # question's K/V rows stored into its own slot of a pool sized for its longest question.
@@ -405,6 +417,8 @@ def main():
             "algorithmic_flops_per_launch": flops,
             "call_ms": pre_avg,
             "call_tflops": tflops,
+            "back_to_back_call_ms": pre_b2b_ms if do_pre else None,
+            "back_to_back_tflops": flops / (pre_b2b_ms * 1e-3) / 1e12 if do_pre else None,
         },
         "decode": {
             "value": gbps, "unit": "GB/s", "ms": dec_avg,
