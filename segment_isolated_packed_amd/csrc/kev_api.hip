@@ -135,7 +135,8 @@ int32_t prefill_order(int32_t total_tokens, int32_t head_dim, int32_t dtype) {
 
 // Schedule on the device into the (device, stream) workspace.
 int run_schedule(const int32_t *cu, int32_t n_seg, int32_t total_tokens, int32_t block_rows,
-                 int32_t order, hipStream_t stream, int32_t **ws_out, ScheduleLayout *lay_out) {
+                 int32_t order, hipStream_t stream, int32_t **ws_out, ScheduleLayout *lay_out,
+                 const int32_t *prefix_lens = nullptr) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
     int32_t *err = nullptr;
@@ -149,7 +150,7 @@ int run_schedule(const int32_t *cu, int32_t n_seg, int32_t total_tokens, int32_t
     rc = workspace(state().sched_ws, dev, stream, (size_t)lay.total * sizeof(int32_t), &ws);
     if (rc) return rc;
     ScheduleArgs sa{cu, n_seg, total_tokens, block_rows, (int32_t)hist_len, order, n_max,
-                    static_cast<int32_t *>(ws), err};
+                    static_cast<int32_t *>(ws), err, prefix_lens};
     rc = to_status(launch_schedule(sa, stream));
     if (rc) return rc;
     *ws_out = static_cast<int32_t *>(ws);
@@ -191,7 +192,7 @@ int prefill_impl(const void *q, const void *k, const void *v, const int32_t *cu_
     int32_t *ws = nullptr;
     ScheduleLayout lay;
     int rc = run_schedule(cu_seqlens, n_seg, total_tokens, br, prefill_order(total_tokens, head_dim, dtype),
-                          stream, &ws, &lay);
+                          stream, &ws, &lay, pre ? pre->prefix_lens : nullptr);
     if (rc) return rc;
     if (total_tokens == 0) return KEV_OK;   // only empty questions; cu_seqlens still checked
 

@@ -60,6 +60,9 @@ struct ScheduleArgs {
     int64_t n_max_items;      // item capacity the workspace was laid out for
     int32_t *ws;              // workspace, see schedule_layout()
     int32_t *err;             // device error word
+    // chunked prefill: rows already cached per question; with at most 64 questions the
+    // question order then follows the blocks of prefix + chunk (the work of the last block)
+    const int32_t *prefix_lens;
 };
 
 // Item orders.  Question-major: questions in descending length, query block t descending

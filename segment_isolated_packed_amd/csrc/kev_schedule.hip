@@ -221,12 +221,18 @@ __global__ __launch_bounds__(64) void schedule_small_kernel(ScheduleArgs a) {
         }
         return;
     }
-    // rank: position in descending block count (ties by index); before: items of the questions
-    // ranked ahead (question-major offset of this question's first item)
+    // rank: position in descending order key (ties by index); before: items of the questions
+    // ranked ahead (question-major offset of this question's first item).  The key is the
+    // block count, or for chunks continuing a cached prefix the blocks of prefix + chunk, so
+    // that the questions whose items read the most keys come first.
+    int key = nb;
+    if (a.prefix_lens && a.order != kOrderLevel && lane < a.n_seg && nb > 0)   // level-major needs nb order
+        key = qblocks(max(a.prefix_lens[lane], 0) + len, a.block_rows);
     int rank = 0, before = 0, maxnb = 0;
     for (int j = 0; j < a.n_seg; ++j) {
         const int nj = __builtin_amdgcn_readlane(nb, j);
-        const bool ahead = nj > nb || (nj == nb && j < lane);
+        const int kj = __builtin_amdgcn_readlane(key, j);
+        const bool ahead = kj > key || (kj == key && j < lane);
         rank += ahead ? 1 : 0;
         before += ahead ? nj : 0;
         maxnb = max(maxnb, nj);
