@@ -93,6 +93,10 @@ def main():
     ap.add_argument("--workload", default="qwen25_7b",
                     choices=["qwen25_7b", "qwen3_8b", "skewed_long"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--back-to-back", action="store_true",
+                    help="also time 100 prefill calls per event pair (throughput of calls issued "
+                         "one after another; off by default so that profiler averages of the "
+                         "attention kernel cover the timed and roofline calls only)")
     ap.add_argument("--no-extra-legs", action="store_true",
                     help="time only the prefill and decode calls of the step (profiling runs whose "
                          "per-kernel averages must not mix in the other legs' launches)")
@@ -203,7 +207,7 @@ def main():
         # Back-to-back calls (one event pair around 100 launches, 5 repeats, median): the
         # throughput a caller issuing prefills one after another sees.
         b2b = []
-        for _ in range(5):
+        for _ in range(5 if args.back_to_back else 0):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(100):
@@ -211,7 +215,7 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             b2b.append(e0.elapsed_time(e1) / 100)
-        pre_b2b_ms = float(np.median(b2b))
+        pre_b2b_ms = float(np.median(b2b)) if b2b else None
 
     # Prefill-to-slot handoff (kev_packed_attn_prefill_slots) on the same workload: every
     # question's K/V rows stored into its own slot of a pool sized for its longest question.
@@ -418,7 +422,7 @@ def main():
             "call_ms": pre_avg,
             "call_tflops": tflops,
             "back_to_back_call_ms": pre_b2b_ms if do_pre else None,
-            "back_to_back_tflops": flops / (pre_b2b_ms * 1e-3) / 1e12 if do_pre else None,
+            "back_to_back_tflops": flops / (pre_b2b_ms * 1e-3) / 1e12 if do_pre and pre_b2b_ms else None,
         },
         "decode": {
             "value": gbps, "unit": "GB/s", "ms": dec_avg,
