@@ -42,7 +42,8 @@ def test_slot_decode_config(orc, full_case):
 
 
 @pytest.mark.parametrize("hq,hk,d", [(32, 8, 128), (8, 8, 128), (16, 8, 128), (64, 8, 128), (256, 8, 128),
-                                     (28, 4, 128), (8, 2, 64), (4, 1, 64)])
+                                     (28, 4, 128), (8, 2, 64), (4, 1, 64), (32, 2, 128), (32, 1, 64),
+                                     (24, 8, 128)])
 def test_head_layouts_and_edges(orc, hq, hk, d):
     lens = [1, 2, 255, 256, 257, 511, 512, 513, 1000, 1023, 1024, 1025]
     dc = W.make_decode(n_req=len(lens), n_slots=20, capacity=1025, heads=hq, kv_heads=hk,

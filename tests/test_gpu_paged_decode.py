@@ -133,3 +133,36 @@ def test_invalid_blocks_and_lengths(orc, monkeypatch):
         with pytest.raises(K.KevError) as e:
             K.kev_paged_attn_decode(**b)
         assert e.value.code == code
+
+
+def test_block_table_limit(orc):
+    """One position per block and a request spanning KEV_PAGED_MAX_BLOCKS blocks: the whole
+    block-id table of that request is staged on chip.  A request one position longer, with a
+    table row wide enough to hold it, is past the limit and is flagged and skipped."""
+    lim = K.KEV_PAGED_MAX_BLOCKS
+    rng = np.random.default_rng(64)
+    hq, hk, d = 8, 2, 64
+    lens = np.array([lim, 1000, 1, lim + 1], np.int32)
+    used = int(lens[:3].sum())
+    n_blocks = used + 3
+    pool = W.round_to_bf16_bits(rng.standard_normal((n_blocks, 2, hk, 1, d)).astype(np.float32))
+    perm = rng.permutation(n_blocks).astype(np.int32)
+    tables = np.full((4, lim + 1), -1, np.int32)
+    off = 0
+    for r in range(3):
+        tables[r, :lens[r]] = perm[off:off + lens[r]]
+        off += int(lens[r])
+    tables[3, :] = 0                           # never read: the request is past the limit
+    q, kn, vn = (W.round_to_bf16_bits(rng.standard_normal((4, h, d)).astype(np.float32)) for h in (hq, hk, hk))
+    pc = W.PagedDecodeCase("table_limit", hq, hk, d, 1, 64, tables, lens, q, kn, vn, pool)
+    say(f"paged decode B=1, table limit {lim}, lens={list(lens)}")
+    out0 = torch.zeros((4, hq, d), dtype=torch.bfloat16, device="cuda")
+    a = paged_dev(pc)
+    out = K.kev_paged_attn_decode(**a, out=out0)
+    assert K.kev_get_device_errors() == K.KEV_DEVERR_CACHE_LEN
+    got = to_host_f64(out)
+    assert (got[3] == 0).all()
+    ref, ref_pool = orc.paged_decode(q[:3], pool, tables[:3], lens[:3], kn[:3], vn[:3], hq, W.BF16,
+                                     want_pool=True)
+    assert_parity(got[:3], ref, W.BF16, "paged decode at the block-table limit")
+    assert np.array_equal(to_host_bits(a["kv_pool"]), ref_pool)

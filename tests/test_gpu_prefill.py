@@ -67,7 +67,7 @@ def test_skewed_long_sampled(orc):
 
 
 @pytest.mark.parametrize("hq,hk", [(28, 4), (32, 8), (7, 1), (4, 1), (8, 8), (16, 2), (12, 4),
-                                   (5, 1), (6, 1), (2, 1), (64, 8), (3, 3)])
+                                   (5, 1), (6, 1), (2, 1), (64, 8), (3, 3), (32, 2), (32, 1), (24, 4)])
 def test_head_layouts(orc, hq, hk):
     case = W.make_prefill([1, 95, 31, 160, 64, 33, 0, 200], hq, hk, 128, W.BF16, seed=hq * 100 + hk)
     check_full(case, orc, f"bf16 {hq}/{hk} d128 ragged")
