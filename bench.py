@@ -307,6 +307,35 @@ def main():
         if K.kev_get_device_errors():
             raise RuntimeError("device error flags in the low-occupancy decode leg")
 
+    # Decode time against bytes: the decode workload with every length scaled by f (the appends
+    # land at the scaled rows, after every other decode leg has run).  A line through the
+    # points splits a call into a fixed cost and a steady streaming rate.
+    scale_res = None
+    if extra and do_dec:
+        log("decode time vs bytes")
+        pts = []
+        for f in (0.125, 0.25, 0.5, 0.75, 1.0):
+            L = np.maximum(1, np.round(dc.cache_lens * f)).astype(np.int32)
+            slens = torch.from_numpy(L).to(dev)
+            sbytes = int((L.astype(np.int64) - 1).sum()) * dc.kv_heads * dc.head_dim * 2 * 2 + \
+                dc.n_req * (dc.kv_heads * dc.head_dim * 2 * 2 * 2 + dc.heads * dc.head_dim * 2 * 2)
+            sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+            for i in range(max(args.warmup, 1) + args.steps):
+                torch.sum(flush_rows, dim=1, dtype=torch.int32, out=flush_sink)
+                e = sev[i - max(args.warmup, 1)] if i >= max(args.warmup, 1) else None
+                if e: e[0].record(stream)
+                K.kev_slot_attn_decode(dq, dpool, dids, slens, dkn, dvn, out=dout)
+                if e: e[1].record(stream)
+            torch.cuda.synchronize()
+            pts.append((f, sbytes, float(np.mean([e[0].elapsed_time(e[1]) for e in sev])) * 1e3))
+        if K.kev_get_device_errors():
+            raise RuntimeError("device error flags in the decode scaling leg")
+        slope, icpt = np.polyfit([p[1] for p in pts], [p[2] for p in pts], 1)
+        scale_res = {"length_scales": [p[0] for p in pts], "algorithmic_mb": [p[1] / 1e6 for p in pts],
+                     "us": [p[2] for p in pts], "fixed_us": float(icpt),
+                     "steady_gbps": float(1e-3 / slope) if slope > 0 else None,
+                     "note": "least-squares line: call time = fixed_us + bytes / steady rate (MALL flushed)"}
+
     # The other prefill configurations (parity-test cases; reported for context, not `value`).
     other_res = {}
     if extra and do_pre:
@@ -441,6 +470,7 @@ def main():
         "chunked_prefill": chunk_res,
         "paged_decode": paged_res or None,
         "decode_low_occupancy": low_res or None,
+        "decode_time_vs_bytes": scale_res,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and do_pre:
