@@ -43,7 +43,7 @@
 // already issued on MFMA.  The wavefront waits for its own loads of K(j+1) and
 // V(j), meets the others at one barrier (which also retires all reads of K(j)
 // and V(j-1), so their stages take K(j+4) and V(j+3)), reads every fragment of
-// K(j+1) and V(j) into registers at once, takes the softmax of tile j while
+// V(j) and then K(j+1) into registers at once, takes the softmax of tile j while
 // those reads land, runs P.V of tile j and issues the scores of tile j+1, which
 // execute while it waits at the next barrier.  The loop is unrolled by the
 // stage count, so all LDS addresses carry the stage as an immediate offset.
@@ -386,7 +386,7 @@ void prefill_bf16_kernel(PrefillArgs p) {
     }
 
     // Iteration j: the scores of tile j are in flight on MFMA.  After the barrier the wave
-    // reads all fragments of K(j+1) and V(j) at once, takes the softmax of tile j while
+    // reads all fragments of V(j) and K(j+1) at once, takes the softmax of tile j while
     // those reads land, runs P.V of tile j and issues the scores of tile j+1, which then
     // execute while the wave waits at the next barrier.
     // The loop is unrolled by NS so every stage address is a compile-time offset.
@@ -400,12 +400,14 @@ void prefill_bf16_kernel(PrefillArgs p) {
         if (j < my_tiles) {
             const lds_t *kn = kst((u + 1) % NS);   // past the last tile: an unused read
             const lds_t *vc = vst(u);
-#pragma unroll
-            for (int dc = 0; dc < C::DC; ++dc) kf[dc] = k_frag<D>(kn, dc);
+            // V(j) first: LDS reads return in order, and P.V of tile j needs them before the
+            // scores of tile j+1 need K(j+1).
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) vf[cc * C::DB + db] = vt_frag<D>(vc, cc, db);
+#pragma unroll
+            for (int dc = 0; dc < C::DC; ++dc) kf[dc] = k_frag<D>(kn, dc);
             if (j >= n_full) mask_tile<D>(s, j * KT, P + qrow, P + L);
             tile_max<D>(s, c, st);
             apply_rescale<D>(st);
