@@ -47,6 +47,8 @@ CASES = [
     ([96, 1, 50], [64, 300, 17], 32, 8, 64, 320),
     ([31, 32, 33, 0, 5], [1, 63, 0, 10, 257], 28, 4, 128, 300),          # Qwen2.5-7B group of 7
     ([3] * 70, None, 8, 1, 64, 110),                                      # more than 64 questions
+    ([5, 40, 1], [100, 0, 31], 32, 1, 64, 160),                           # group of 32, d 64
+    ([33, 64], [64, 200], 32, 2, 128, 300),                               # group of 16
 ]
 
 

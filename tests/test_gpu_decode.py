@@ -179,6 +179,30 @@ def test_split_units_match_oracle(orc, monkeypatch, splits, paged):
     assert_parity(to_host_f64(out), ref, dc.dtype, f"decode split={splits} paged={paged}")
 
 
+@pytest.mark.parametrize("hq,hk,d", [(32, 1, 128), (32, 2, 64), (28, 4, 128)])
+@pytest.mark.parametrize("paged", [False, True])
+def test_split_merge_wide_groups(orc, monkeypatch, hq, hk, d, paged):
+    """Split units whose group has 7, 16 or 32 query heads: the merge combines every head's
+    ranges (32 heads x 128 d is more output than one merge workgroup covers in one pass)."""
+    lens = [3, 64, 700, 1025]
+    dc = W.make_decode(n_req=len(lens), n_slots=6, capacity=1025, heads=hq, kv_heads=hk, head_dim=d,
+                       seed=90 + hq + hk, cache_lens=lens)
+    monkeypatch.setenv("KEV_DECODE_SPLITS", "5")
+    say(f"decode split=5 {hq}/{hk} d{d} paged={paged}")
+    ref, ref_pool = orc.decode_case(dc, want_pool=True)
+    if paged:
+        pc = W.paged_from_slots(dc, 32, spare_blocks=3)
+        t = dict(q=to_dev(pc.q, W.BF16), kv_pool=to_dev(pc.pool, W.BF16), block_tables=to_dev_i32(pc.block_tables),
+                 cache_lens=to_dev_i32(pc.cache_lens), k_new=to_dev(pc.k_new, W.BF16), v_new=to_dev(pc.v_new, W.BF16))
+        out = K.kev_paged_attn_decode(**t)
+        torch.cuda.synchronize()
+    else:
+        out, pool = run(dc)
+        assert np.array_equal(to_host_bits(pool), ref_pool)
+    assert K.kev_get_device_errors() == 0
+    assert_parity(to_host_f64(out), ref, dc.dtype, f"decode split=5 {hq}/{hk} d{d} paged={paged}")
+
+
 @pytest.mark.parametrize("n_req", [1, 2, 5])
 def test_low_occupancy_batches(orc, n_req):
     """A batch that has shrunk to a few requests (automatic split count)."""
