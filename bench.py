@@ -1,21 +1,24 @@
 """Benchmark of the packed-prefill + slot-decode hot path on one MI355X.
 
-One step = one packed prefill over the Qwen2.5-7B-shaped workload (bf16, 28 q / 4 kv
-heads, head_dim 128, 8 questions with lengths uniform in [256, 2048], seed 42) followed
-by one slot-pool decode (bf16, 32 q / 8 kv heads, 64 requests, slot capacity 2458,
-80-slot pool, new K/V appended in-kernel, seed 44).  Between the two a 512 MiB buffer is
-read so the decode reads its KV rows from HBM rather than from the 256 MB MALL.
+One step = one packed prefill over the skewed long workload (bf16, 32 q / 8 kv heads,
+head_dim 128, 131072 tokens over 256 questions: 90% of lengths in [16,128], 10% in
+[2048,8192], seed 45) followed by one slot-pool decode (bf16, 32 q / 8 kv heads, 64
+requests, slot capacity 2458, 80-slot pool, new K/V appended in-kernel, seed 44).  Between
+the two a 512 MiB buffer is read so the decode reads its KV rows from HBM rather than from
+the 256 MB MALL.  ``--workload`` selects another prefill shape for the step.
 
 Prints ONE JSON line.  `value` is the prefill's effective TFLOP/s (only unmasked score
-entries counted: 4 * d * heads * sum L(L+1)/2 FLOPs per call) over the average duration
-of the prefill call (work-list pass + attention kernel) measured with HIP events on the
-launch stream; `roofline.achieved` divides the same FLOPs by the attention kernel's own
-average duration, taken with events the library records around that launch.  The decode's
-achieved HBM GB/s (algorithmic bytes over event-timed duration) is reported beside it,
-and so are more calls timed the same way: the prefill that also stores every question's K/V
-into its slot, a chunked prefill of 8 long prompts against their cached prefixes, the
-decode over a paged (block-table) pool holding the same rows, and the decode of batches cut
-to 1, 4 and 16 requests (low occupancy).
+entries counted: 4 * d * heads * sum L(L+1)/2 FLOPs per call) over the average duration of
+the prefill call (work-list pass + attention kernel) measured with HIP events on the launch
+stream; `roofline.achieved` divides the same FLOPs by the attention kernel's own average
+duration, taken with events the library records around that launch on the call's stream.
+The decode's achieved HBM GB/s (algorithmic bytes over event-timed duration) is reported
+beside it, per call and per kernel.  More calls are timed the same way: the other prefill
+shapes, the prefill that also stores every question's K/V into its slot, a chunked prefill
+of 8 long prompts against their cached prefixes, the decode over a paged (block-table)
+pool holding the same rows, the decode of batches cut to 1, 4 and 16 requests, and the
+decode at scaled lengths (fixed cost and streaming rate per call).  The CPU oracle is
+timed on the host cores on bounded samples of every prefill shape.
 """
 from __future__ import annotations
 
@@ -32,26 +35,17 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBPS = 8000.0        # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-# sources whose change invalidates a kernel's recorded HBM traffic
-PREFILL_SOURCES = ["kev_prefill_bf16.hip", "kev_mfma_core.h", "kev_internal.h"]
-DECODE_SOURCES = ["kev_decode.hip", "kev_mfma_core.h", "kev_internal.h"]
+# Sources whose change invalidates a kernel's recorded HBM traffic: the kernel itself and
+# everything that decides its launch and item order (the work-list pass and the call).
+PREFILL_SOURCES = ["kev_prefill_bf16.hip", "kev_mfma_core.h", "kev_internal.h", "kev_schedule.hip",
+                   "kev_api.hip"]
+DECODE_SOURCES = ["kev_decode.hip", "kev_mfma_core.h", "kev_internal.h", "kev_api.hip"]
+STORE_SOURCES = ["kev_store_kv.hip", "kev_internal.h", "kev_api.hip"]
+PREFILL_NAMES = ("qwen25_7b", "qwen3_8b", "skewed_long")
 
 
 def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
-
-
-def traffic_for(kernel: str, src_hash: str):
-    """HBM bytes per launch from committed rocprofv3 PMC summaries, if the kernel is unchanged."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    e = t.get(kernel)
-    if not e or e.get("source_sha256") != src_hash:
-        return None
-    return e.get("bytes_per_launch")
 
 
 def source_hash(files) -> str:
@@ -63,36 +57,101 @@ def source_hash(files) -> str:
     return h.hexdigest()
 
 
-def cpu_baseline(case, budget_s: float = 10.0) -> dict:
-    """The oracle as it stands, timed on the host cores: whole prefill calls over the full
-    workload (all questions, all heads), repeated until about budget_s seconds have passed."""
-    import oracle
-    orc = oracle.get()
-    calls = 0
+def traffic_for(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of
+    `kernel` on `workload`, or None if there is none or the sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(f"{kernel}/{workload}")
+    if not e or e.get("source_sha256") != src_hash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def _sample_pairs(case, rng, n):
+    """n (row, head) pairs drawn uniformly over the workload, with their effective FLOPs."""
+    import numpy as np
+    rows = rng.integers(0, case.total_tokens, n).astype(np.int32)
+    heads = rng.integers(0, case.heads, n).astype(np.int32)
+    seg = np.searchsorted(case.cu_seqlens, rows, side="right") - 1
+    keys = rows - case.cu_seqlens[seg] + 1
+    return rows, heads, int(4 * case.head_dim * int(keys.astype(np.int64).sum()))
+
+
+def time_oracle_rows(orc, case, budget_s: float, n_threads: int, chunk: int = 4096) -> dict:
+    """The oracle on (row, head) pairs sampled uniformly from the workload, chunk by chunk
+    until about budget_s seconds of compute have passed."""
+    import numpy as np
+    rng = np.random.default_rng(1234)
+    flops = pairs = 0
+    dt = 0.0
+    while dt < budget_s:
+        rows, heads, f = _sample_pairs(case, rng, chunk)
+        t0 = time.perf_counter()
+        orc.prefill_rows(case.q, case.k, case.v, case.cu_seqlens, case.heads, case.kv_heads,
+                         case.head_dim, case.dtype, rows, heads, n_threads=n_threads)
+        dt += time.perf_counter() - t0
+        flops += f
+        pairs += chunk
+    return {"tflops": flops / dt / 1e12, "seconds": dt, "threads": n_threads,
+            "sample": f"{pairs} (row, query head) outputs drawn uniformly over the workload, "
+                      f"{flops / 1e9:.1f} GFLOP effective"}
+
+
+def time_oracle_full(orc, case, n_threads: int) -> dict:
     t0 = time.perf_counter()
-    while True:
-        orc.prefill(case.q, case.k, case.v, case.cu_seqlens, case.heads, case.kv_heads,
-                    case.head_dim, case.dtype)
-        calls += 1
-        dt = time.perf_counter() - t0
-        if dt >= budget_s or calls >= 20:
-            break
-    flops = case.effective_flops() * calls
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": orc.max_threads(),
-            "kind": "oracle",
-            "sample": f"fp64 oracle, {calls} full prefill call(s) over the whole workload "
-                      f"({case.n_seg} questions, {case.heads} heads, "
-                      f"{case.effective_flops() / 1e9:.1f} GFLOP effective each), {dt:.1f} s"}
+    orc.prefill(case.q, case.k, case.v, case.cu_seqlens, case.heads, case.kv_heads, case.head_dim,
+                case.dtype, n_threads=n_threads)
+    dt = time.perf_counter() - t0
+    return {"tflops": case.effective_flops() / dt / 1e12, "seconds": dt, "threads": n_threads,
+            "sample": f"whole workload ({case.n_seg} questions, {case.heads} heads, "
+                      f"{case.effective_flops() / 1e9:.2f} GFLOP effective)"}
+
+
+def oracle_timing(headline: str, budget_s: float) -> tuple[dict, dict]:
+    """The oracle as it stands, on the host cores: threaded over all cores on every prefill
+    shape (whole workload where it takes seconds, uniform row samples otherwise) and
+    single-threaded on the tiny and Qwen2.5-7B shapes.  Returns (cpu_baseline of the
+    headline workload, every timing)."""
+    import oracle
+    from segment_isolated_packed_amd import workloads as W
+    orc = oracle.get()
+    cores = orc.max_threads()          # read before any single-threaded call changes it
+    res = {"cores": cores}
+    tiny = W.prefill_case("tiny")
+    res["tiny"] = {"threaded": time_oracle_full(orc, tiny, cores),
+                   "single_thread": time_oracle_full(orc, tiny, 1)}
+    for name in PREFILL_NAMES:
+        log(f"oracle timing: {name}")
+        c = W.prefill_case(name)
+        entry = {}
+        if name == "skewed_long":
+            entry["threaded"] = time_oracle_rows(orc, c, budget_s, cores)
+        else:
+            entry["threaded"] = time_oracle_full(orc, c, cores)
+        if name == "qwen25_7b":
+            entry["single_thread"] = time_oracle_rows(orc, c, budget_s / 3, 1, chunk=256)
+        res[name] = entry
+        del c
+    h = res[headline]["threaded"]
+    base = {"value": h["tflops"], "unit": "TFLOP/s", "cores": h["threads"], "kind": "oracle",
+            "sample": f"fp64 oracle ({W.PREFILL_DESCRIPTIONS[headline]}): {h['sample']}, "
+                      f"{h['seconds']:.1f} s on {h['threads']} threads"}
+    return base, res
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen25_7b",
-                    choices=["qwen25_7b", "qwen3_8b", "skewed_long"])
+    ap.add_argument("--workload", default="skewed_long", choices=list(PREFILL_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--oracle-budget", type=float, default=20.0,
+                    help="seconds of oracle compute per sampled leg")
     ap.add_argument("--back-to-back", action="store_true",
                     help="also time 100 prefill calls per event pair (throughput of calls issued "
                          "one after another; off by default so that profiler averages of the "
@@ -127,6 +186,16 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+    def new_events(n, k):
+        """n groups of k timing events, each recorded once so the HIP events exist before
+        their handles are handed to the library."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(k)] for _ in range(n)]
+        for g in evs:
+            for e in g:
+                e.record()
+        torch.cuda.synchronize()
+        return evs
+
     if args.only == "copy":
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -145,6 +214,16 @@ def main():
         q, k, v = (to_dev(x, pc.dtype) for x in (pc.q, pc.k, pc.v))
         cu = torch.from_numpy(pc.cu_seqlens).to(dev)
         out = torch.empty_like(q)
+    flush_buf = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+    flush_rows = flush_buf.view(torch.int32).view(512, 1 << 18)   # summed in place: read only
+    flush_sink = torch.zeros(512, dtype=torch.int32, device=dev)
+
+    def flush():
+        if args.flush == "read":
+            torch.sum(flush_rows, dim=1, dtype=torch.int32, out=flush_sink)
+        elif args.flush == "write":
+            flush_buf.fill_(1)
+
     if do_dec:
         log("generating slot-decode inputs")
         dc = W.make_decode()
@@ -152,9 +231,6 @@ def main():
         dids = torch.from_numpy(dc.slot_ids).to(dev)
         dlens = torch.from_numpy(dc.cache_lens).to(dev)
         dout = torch.empty_like(dq)
-        flush_buf = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
-        flush_rows = flush_buf.view(torch.int32).view(512, 1 << 18)   # summed in place: read only
-        flush_sink = torch.zeros(512, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -163,10 +239,7 @@ def main():
             K.kev_packed_attn_prefill(q, k, v, cu, out=out)
             if ev: ev[1].record(stream)
         if do_dec:
-            if args.flush == "read":
-                torch.sum(flush_rows, dim=1, dtype=torch.int32, out=flush_sink)
-            elif args.flush == "write":
-                flush_buf.fill_(1)
+            flush()
             if ev: ev[2].record(stream)
             K.kev_slot_attn_decode(dq, dpool, dids, dlens, dkn, dvn, out=dout)
             if ev: ev[3].record(stream)
@@ -179,7 +252,7 @@ def main():
     if errs:
         raise RuntimeError(f"device error flags {errs}")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = new_events(args.steps, 4)
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -189,21 +262,19 @@ def main():
     wall = time.perf_counter() - t0
     log("timed region done")
 
-    # The attention kernel alone (roofline): the same prefill calls again, with events that the
-    # library records around that kernel's launch (kept out of the timed steps, whose call
-    # times they would lengthen).
-    kevents = []
+    # The main kernels alone (roofline): the same calls again, with events that the library
+    # records around that kernel's launch on the call's stream (kept out of the timed steps,
+    # whose call times they would lengthen).
+    pre_kernel_ms = dec_kernel_ms = float("nan")
+    pre_b2b_ms = None
     if do_pre:
-        kevents = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for evs in kevents:     # create the HIP events before their handles are passed on
-            for e in evs:
-                e.record(stream)
-        torch.cuda.synchronize()
-        for e in kevents:
+        kev = new_events(args.steps, 2)
+        for e in kev:
             K.kev_set_kernel_events(e[0], e[1])
             K.kev_packed_attn_prefill(q, k, v, cu, out=out)
             K.kev_set_kernel_events(None, None)
         torch.cuda.synchronize()
+        pre_kernel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in kev]))
         # Back-to-back calls (one event pair around 100 launches, 5 repeats, median): the
         # throughput a caller issuing prefills one after another sees.
         b2b = []
@@ -216,19 +287,31 @@ def main():
             torch.cuda.synchronize()
             b2b.append(e0.elapsed_time(e1) / 100)
         pre_b2b_ms = float(np.median(b2b)) if b2b else None
+    if do_dec:
+        kev = new_events(args.steps, 2)
+        for e in kev:
+            flush()
+            K.kev_set_kernel_events(e[0], e[1])
+            K.kev_slot_attn_decode(dq, dpool, dids, dlens, dkn, dvn, out=dout)
+            K.kev_set_kernel_events(None, None)
+        torch.cuda.synchronize()
+        dec_kernel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in kev]))
+    if K.kev_get_device_errors():
+        raise RuntimeError("device error flags in the kernel-timing pass")
 
-    # Prefill-to-slot handoff (kev_packed_attn_prefill_slots) on the same workload: every
-    # question's K/V rows stored into its own slot of a pool sized for its longest question.
-    slots_res = None
     extra = not args.no_extra_legs
+
+    # Prefill-to-slot handoff (kev_packed_attn_prefill_slots) on the step's prefill workload:
+    # every question's K/V rows stored into its own slot of a pool sized for its longest
+    # question.  The store kernel's own duration comes from the profiler trace, not from here.
+    slots_res = None
     if extra and do_pre and pc.dtype == W.BF16:
         cap = int(max(pc.seqlens.max(), 1))
         spool = torch.zeros((pc.n_seg + 4, 2, pc.kv_heads, cap, pc.head_dim), dtype=torch.bfloat16, device=dev)
         sids = torch.arange(pc.n_seg, dtype=torch.int32, device=dev)
         for _ in range(2):
             K.kev_packed_attn_prefill_slots(q, k, v, cu, spool, sids, out=out)
-        torch.cuda.synchronize()
-        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        sev = new_events(args.steps, 2)
         for e in sev:
             e[0].record(stream)
             K.kev_packed_attn_prefill_slots(q, k, v, cu, spool, sids, out=out)
@@ -236,9 +319,11 @@ def main():
         torch.cuda.synchronize()
         if K.kev_get_device_errors():
             raise RuntimeError("device error flags in the prefill-to-slot leg")
-        slots_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in sev]))
-        store_bytes = 2 * 2 * pc.total_tokens * pc.kv_heads * pc.head_dim * 2   # K and V, read + write
-        slots_res = {"ms": slots_ms, "store_bytes": store_bytes, "slot_capacity": cap}
+        s_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in sev]))
+        slots_res = {"ms": s_ms, "store_bytes": 2 * 2 * pc.total_tokens * pc.kv_heads * pc.head_dim * 2,
+                     "slot_capacity": cap,
+                     "call": "kev_packed_attn_prefill_slots: prefill + every question's K/V stored "
+                             "into its slot (store_kv_kernel, timed in the profiler trace)"}
         del spool
 
     # The decode over a paged pool (kev_paged_attn_decode): the same requests and rows cut into
@@ -251,12 +336,9 @@ def main():
             ppool, pq, pkn, pvn = (to_dev(x, W.BF16) for x in (pg.pool, pg.q, pg.k_new, pg.v_new))
             ptab, plen = (torch.from_numpy(x).to(dev) for x in (pg.block_tables, pg.cache_lens))
             pout = torch.empty_like(pq)
-            pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+            pev = new_events(args.steps, 2)
             for i in range(max(args.warmup, 1) + args.steps):
-                if args.flush == "read":
-                    torch.sum(flush_rows, dim=1, dtype=torch.int32, out=flush_sink)
-                elif args.flush == "write":
-                    flush_buf.fill_(1)
+                flush()
                 e = pev[i - max(args.warmup, 1)] if i >= max(args.warmup, 1) else None
                 if e: e[0].record(stream)
                 K.kev_paged_attn_decode(pq, ppool, ptab, plen, pkn, pvn, out=pout)
@@ -265,12 +347,11 @@ def main():
             if K.kev_get_device_errors():
                 raise RuntimeError("device error flags in the paged-decode leg")
             ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
-            reserved = pg.n_blocks * B
             paged_res.append({
                 "block_size": B, "ms": ms, "gbps": pg.algorithmic_bytes() / (ms * 1e-3) / 1e9,
                 "algorithmic_mb": pg.algorithmic_bytes() / 1e6, "blocks": pg.n_blocks,
                 "pool_mb": pg.pool.nbytes / 1e6, "slot_pool_mb": dc.pool.nbytes / 1e6,
-                "rows_used": int(dc.cache_lens.sum()), "rows_reserved_paged": reserved,
+                "rows_used": int(dc.cache_lens.sum()), "rows_reserved_paged": pg.n_blocks * B,
                 "rows_reserved_slots": dc.n_slots * dc.capacity})
             del ppool, pq, pkn, pvn, pout
 
@@ -290,9 +371,9 @@ def main():
             for mode in ("auto", "unsplit"):
                 if mode == "unsplit":
                     os.environ["KEV_DECODE_SPLITS"] = "1"
-                lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+                lev = new_events(args.steps, 2)
                 for i in range(max(args.warmup, 1) + args.steps):
-                    torch.sum(flush_rows, dim=1, dtype=torch.int32, out=flush_sink)
+                    flush()
                     e = lev[i - max(args.warmup, 1)] if i >= max(args.warmup, 1) else None
                     if e: e[0].record(stream)
                     K.kev_slot_attn_decode(lq, dpool, lids, llens, lkn, lvn, out=lout)
@@ -319,9 +400,9 @@ def main():
             slens = torch.from_numpy(L).to(dev)
             sbytes = int((L.astype(np.int64) - 1).sum()) * dc.kv_heads * dc.head_dim * 2 * 2 + \
                 dc.n_req * (dc.kv_heads * dc.head_dim * 2 * 2 * 2 + dc.heads * dc.head_dim * 2 * 2)
-            sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+            sev = new_events(args.steps, 2)
             for i in range(max(args.warmup, 1) + args.steps):
-                torch.sum(flush_rows, dim=1, dtype=torch.int32, out=flush_sink)
+                flush()
                 e = sev[i - max(args.warmup, 1)] if i >= max(args.warmup, 1) else None
                 if e: e[0].record(stream)
                 K.kev_slot_attn_decode(dq, dpool, dids, slens, dkn, dvn, out=dout)
@@ -336,10 +417,10 @@ def main():
                      "steady_gbps": float(1e-3 / slope) if slope > 0 else None,
                      "note": "least-squares line: call time = fixed_us + bytes / steady rate (MALL flushed)"}
 
-    # The other prefill configurations (parity-test cases; reported for context, not `value`).
+    # The other prefill shapes (parity-test cases; reported beside `value`, not as it).
     other_res = {}
     if extra and do_pre:
-        for name in ("qwen3_8b", "skewed_long"):
+        for name in PREFILL_NAMES:
             if name == args.workload:
                 continue
             log(f"prefill {name}")
@@ -349,11 +430,7 @@ def main():
             oout = torch.empty_like(oq)
             for _ in range(2):
                 K.kev_packed_attn_prefill(oq, ok_, ov, ocu, out=oout)
-            oev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(10)]
-            for evs in oev:
-                for e in evs:
-                    e.record(stream)
-            torch.cuda.synchronize()
+            oev = new_events(args.steps, 4)
             for e in oev:
                 e[0].record(stream)
                 K.kev_set_kernel_events(e[2], e[3])
@@ -365,9 +442,12 @@ def main():
                 raise RuntimeError(f"device error flags in the {name} prefill leg")
             cms = float(np.mean([e[0].elapsed_time(e[1]) for e in oev]))
             kms = float(np.mean([e[2].elapsed_time(e[3]) for e in oev]))
+            ktf = oc.effective_flops() / (kms * 1e-3) / 1e12
             other_res[name] = {"tokens": oc.total_tokens, "effective_gflop": oc.effective_flops() / 1e9,
                                "call_ms": cms, "call_tflops": oc.effective_flops() / (cms * 1e-3) / 1e12,
-                               "kernel_ms": kms, "kernel_tflops": oc.effective_flops() / (kms * 1e-3) / 1e12,
+                               "kernel_ms": kms, "kernel_tflops": ktf, "kernel_frac": ktf / PEAK_BF16_TFLOPS,
+                               "kernel_hbm_bytes_per_launch": traffic_for("prefill_bf16_kernel", name,
+                                                                          source_hash(PREFILL_SOURCES)),
                                "workload": W.PREFILL_DESCRIPTIONS[name]}
             del oq, ok_, ov, oout
 
@@ -382,27 +462,30 @@ def main():
         cout = torch.empty_like(cq)
         for _ in range(max(args.warmup, 1)):
             K.kev_chunked_prefill_slots(cq, ck, cv, ccu, cpool, cids, cpre, out=cout)
-        torch.cuda.synchronize()
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        cev = new_events(args.steps, 4)
         for e in cev:
             e[0].record(stream)
+            K.kev_set_kernel_events(e[2], e[3])
             K.kev_chunked_prefill_slots(cq, ck, cv, ccu, cpool, cids, cpre, out=cout)
+            K.kev_set_kernel_events(None, None)
             e[1].record(stream)
         torch.cuda.synchronize()
         if K.kev_get_device_errors():
             raise RuntimeError("device error flags in the chunked-prefill leg")
         c_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in cev]))
+        ck_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in cev]))
         c_tf = cc.effective_flops() / (c_ms * 1e-3) / 1e12
         chunk_res = {
             "ms": c_ms, "effective_tflops": c_tf, "pct_peak": c_tf / PEAK_BF16_TFLOPS * 100,
+            "kernel_ms": ck_ms, "kernel_tflops": cc.effective_flops() / (ck_ms * 1e-3) / 1e12,
             "effective_gflop": cc.effective_flops() / 1e9, "algorithmic_mb": cc.algorithmic_bytes() / 1e6,
             "workload": W.CHUNKED_DESCRIPTION, "seed": cc.seed,
-            "kernel_hbm_bytes_per_launch": traffic_for("prefill_bf16_kernel_prefix", source_hash(PREFILL_SOURCES)),
+            "kernel_hbm_bytes_per_launch": traffic_for("prefill_bf16_kernel_prefix", "chunked_qwen25_7b",
+                                                       source_hash(PREFILL_SOURCES)),
             "call": "kev_chunked_prefill_slots: scheduler + prefill_bf16_kernel<128, prefix> + K/V append"}
         del cq, ck, cv, cpool, cout
 
     pre_ms = [e[0].elapsed_time(e[1]) for e in events] if do_pre else [float("nan")]
-    pre_kernel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in kevents])) if do_pre else float("nan")
     dec_ms = [e[2].elapsed_time(e[3]) for e in events] if do_dec else [float("nan")]
     pre_avg = float(np.mean(pre_ms))
     dec_avg = float(np.mean(dec_ms))
@@ -411,9 +494,8 @@ def main():
     tflops = flops / (pre_avg * 1e-3) / 1e12 if do_pre else None
     kernel_tflops = flops / (pre_kernel_ms * 1e-3) / 1e12 if do_pre else None
     gbps = dbytes / (dec_avg * 1e-3) / 1e9 if do_dec else None
+    dec_kernel_gbps = dbytes / (dec_kernel_ms * 1e-3) / 1e9 if do_dec else None
 
-    pre_hash = source_hash(PREFILL_SOURCES)
-    dec_hash = source_hash(DECODE_SOURCES)
     result = {
         "metric": "effective TFLOP/s packed prefill (% MFMA peak); decode HBM GB/s (% peak)",
         "value": tflops,
@@ -443,39 +525,41 @@ def main():
         "roofline": {
             "bound": "mfma", "achieved": kernel_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": kernel_tflops / PEAK_BF16_TFLOPS if kernel_tflops else None,
-            "traffic": traffic_for("prefill_bf16_kernel", pre_hash),
+            "traffic": traffic_for("prefill_bf16_kernel", args.workload, source_hash(PREFILL_SOURCES)),
             "kernel": "kev prefill_bf16_kernel<128, false> (the attention kernel; events recorded "
                       "by the library around its launch on the call's stream)",
             "kernel_ms": pre_kernel_ms,
             "algorithmic_flops_per_launch": flops,
             "call_ms": pre_avg,
             "call_tflops": tflops,
-            "back_to_back_call_ms": pre_b2b_ms if do_pre else None,
-            "back_to_back_tflops": flops / (pre_b2b_ms * 1e-3) / 1e12 if do_pre and pre_b2b_ms else None,
+            "call_frac": tflops / PEAK_BF16_TFLOPS if tflops else None,
+            "back_to_back_call_ms": pre_b2b_ms,
+            "back_to_back_tflops": flops / (pre_b2b_ms * 1e-3) / 1e12 if pre_b2b_ms else None,
         },
         "decode": {
             "value": gbps, "unit": "GB/s", "ms": dec_avg,
-            "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                         "frac": gbps / PEAK_HBM_GBPS if gbps else None,
-                         "traffic": traffic_for("decode_bf16_kernel", dec_hash),
-                         "kernel": "kev decode_bf16_kernel<128> (one decode call, the only kernel)",
+            "roofline": {"bound": "hbm", "achieved": dec_kernel_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": dec_kernel_gbps / PEAK_HBM_GBPS if dec_kernel_gbps else None,
+                         "kernel_ms": dec_kernel_ms,
+                         "call_gbps": gbps, "call_frac": gbps / PEAK_HBM_GBPS if gbps else None,
+                         "traffic": traffic_for("decode_bf16_kernel", "slot_decode", source_hash(DECODE_SOURCES)),
+                         "kernel": "kev decode_bf16_kernel<128> (the only kernel of the call; kernel "
+                                   "events recorded by the library, MALL flushed before each call)",
                          "algorithmic_bytes_per_launch": dbytes},
         },
-        "prefill_slots": None if slots_res is None else {
-            "ms": slots_res["ms"], "extra_ms_vs_prefill": slots_res["ms"] - pre_avg,
-            "store_bytes": slots_res["store_bytes"], "slot_capacity": slots_res["slot_capacity"],
-            "store_gbps_incl_launch": slots_res["store_bytes"] / max(slots_res["ms"] - pre_avg, 1e-6) / 1e6,
-            "call": "kev_packed_attn_prefill_slots: prefill + every question's K/V stored into its slot"},
+        "prefill_slots": None if slots_res is None else dict(slots_res, extra_ms_vs_prefill=slots_res["ms"] - pre_avg),
         "prefill_other_configs": other_res or None,
         "chunked_prefill": chunk_res,
         "paged_decode": paged_res or None,
         "decode_low_occupancy": low_res or None,
         "decode_time_vs_bytes": scale_res,
         "cpu_baseline": None,
+        "oracle_timing": None,
     }
     if not args.no_cpu_baseline and do_pre:
-        log("timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(pc)
+        log("timing the CPU oracle on bounded samples")
+        del q, k, v, out
+        result["cpu_baseline"], result["oracle_timing"] = oracle_timing(args.workload, args.oracle_budget)
     print(json.dumps(result), flush=True)
 
 

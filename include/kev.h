@@ -42,14 +42,24 @@
  *     enqueues nothing.  n_seg == 0 or n_req == 0 is a successful no-op.
  *   - Device-array contents (cu_seqlens, slot_ids, cache_lens, prefix_lens) are guarded in
  *     the kernels: an invalid unit is skipped (its outputs are left untouched,
- *     nothing out of range is read or written) and a bit is set in the
- *     per-device error word read by kev_get_device_errors.  With the
- *     environment variable KEV_CHECK=1 they are also copied to the host and
- *     checked synchronously before launch, returning the matching status.
- *   - Each (device, stream) pair gets its own workspace, allocated by the
- *     library on first use and grown when needed (this may synchronise the
- *     device).  Calls on one stream are ordered; calls on different streams
- *     do not share workspace.
+ *     nothing out of range is read or written) and a bit is set in the error
+ *     word of the call's (device, stream), read by kev_get_device_errors on that
+ *     stream.  With the environment variable KEV_CHECK=1 they are also copied to
+ *     the host and checked synchronously before launch, returning the matching
+ *     status.
+ *   - Workspace (the prefill's work list, the split decode's partial states)
+ *     is stream-ordered: taken from a library-owned memory pool of the device
+ *     with hipMallocFromPoolAsync on the call's stream and returned with
+ *     hipFreeAsync on the same stream after the call's last kernel, so no call
+ *     synchronises and calls in flight on different streams never share it.
+ *     The pool keeps its memory for later calls.  On a device without the
+ *     stream-ordered allocator (or with KEV_NO_MEMPOOL=1) one cached buffer per
+ *     (device, stream) is used instead; growing it synchronises that stream,
+ *     and calls on one stream must then come from one host thread at a time.
+ *   - The first call on a (device, stream) allocates that stream's error word
+ *     (256 bytes, kept until the process ends).
+ *   - KEV_LOG=1 prints each call's work decomposition (items, splits, workspace
+ *     bytes) to stderr; it synchronises the stream to read the item count.
  *   - Head grouping: query head h reads KV head h / (heads / kv_heads).
  */
 #ifndef KEV_H
@@ -74,7 +84,7 @@ typedef enum {
     KEV_ERR_NO_MEMORY = -7      /* workspace allocation failed */
 } kev_status;
 
-/* Bits of the per-device error word (kev_get_device_errors). */
+/* Bits of the per-stream error word (kev_get_device_errors). */
 #define KEV_DEVERR_SEQLENS 1u   /* cu_seqlens invalid; the prefill call computed nothing */
 #define KEV_DEVERR_SLOT 2u      /* a request's slot id was out of range; request skipped */
 #define KEV_DEVERR_CACHE_LEN 4u /* a request's cache length was outside [1, capacity]; skipped */
@@ -276,8 +286,11 @@ int kev_set_kernel_events(void *start, void *end);
 const char *kev_status_string(int status);
 
 /*
- * Synchronises `stream`, then reads and clears the error word of the current
- * device into *flags_out (a KEV_DEVERR_* bitmask, 0 if every unit was valid).
+ * Reads and clears the error word of (current device, `stream`) into
+ * *flags_out (a KEV_DEVERR_* bitmask, 0 if every unit of every call enqueued
+ * on `stream` since the last read was valid), after all work enqueued on
+ * `stream` before this call; returns once the read is done (synchronises
+ * `stream`).  Flags raised by calls on other streams are not seen here.
  */
 int kev_get_device_errors(void *stream, int32_t *flags_out);
 

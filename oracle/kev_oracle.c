@@ -569,6 +569,7 @@ int kev_oracle_paged_decode(const void *q, const void *pool, int32_t n_blocks, i
         return rc;
     if (n_req < 0 || n_blocks <= 0 || block_size <= 0 || max_blocks <= 0)
         return ORACLE_BAD_ARG;
+    /* every length and block id first: the append check below walks other requests' rows */
     for (int32_t r = 0; r < n_req; r++) {
         int32_t L = cache_lens[r];
         if (L < 1 || (L - 1) / block_size >= max_blocks)
@@ -578,6 +579,9 @@ int kev_oracle_paged_decode(const void *q, const void *pool, int32_t n_blocks, i
             if (b < 0 || b >= n_blocks)
                 return ORACLE_BAD_SLOT;
         }
+    }
+    for (int32_t r = 0; r < n_req; r++) {
+        int32_t L = cache_lens[r];
         int32_t last = block_tables[(size_t)r * max_blocks + (L - 1) / block_size];
         if (paged_row_taken(block_tables, max_blocks, cache_lens, n_req, block_size, r, last,
                             (L - 1) % block_size))

@@ -113,6 +113,26 @@ def _dev_ptr(t, name: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _out_like(q, out):
+    """A new output shaped like q, or the caller's after checking that it is one: the kernels
+    write q.shape elements of q.dtype through the pointer, which the C ABI cannot check."""
+    import torch
+    if out is None:
+        return torch.empty_like(q)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError(f"out must be {tuple(q.shape)} {q.dtype}, got {tuple(out.shape)} {out.dtype}")
+    return out
+
+
+def _total_tokens(T: int, total_tokens):
+    """total_tokens bounds every row the kernels touch, so it may not exceed the tensors' T."""
+    if total_tokens is None:
+        return T
+    if not 0 <= int(total_tokens) <= T:
+        raise ValueError(f"total_tokens must be in [0, {T}] (the rows of q, k, v), got {total_tokens}")
+    return int(total_tokens)
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -136,14 +156,11 @@ def kev_packed_attn_prefill(q, k, v, cu_seqlens, out=None, total_tokens: int | N
         raise TypeError("q, k, v must share one dtype")
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
-    if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("out must match q")
+    out = _out_like(q, out)
+    total_tokens = _total_tokens(T, total_tokens)
     rc = L.kev_packed_attn_prefill(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
                                    _dev_ptr(cu_seqlens, "cu_seqlens"), cu_seqlens.numel() - 1,
-                                   heads, kv_heads, d, _dev_ptr(out, "out"),
-                                   T if total_tokens is None else total_tokens,
+                                   heads, kv_heads, d, _dev_ptr(out, "out"), total_tokens,
                                    _dtype_code(q), _stream(stream))
     _check(rc, "kev_packed_attn_prefill")
     return out
@@ -170,8 +187,7 @@ def kev_slot_attn_decode(q, kv_pool, slot_ids, cache_lens, k_new, v_new, out=Non
     for t in (kv_pool, k_new, v_new):
         if t.dtype != q.dtype:
             raise TypeError("q, kv_pool, k_new, v_new must share one dtype")
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out_like(q, out)
     pool = KvPool(_dev_ptr(kv_pool, "kv_pool").value, n_slots, capacity, kv_heads, d,
                   _dtype_code(kv_pool))
     rc = L.kev_slot_attn_decode(_dev_ptr(q, "q"), ctypes.byref(pool),
@@ -204,8 +220,7 @@ def kev_paged_attn_decode(q, kv_pool, block_tables, cache_lens, k_new, v_new, ou
     for t in (kv_pool, k_new, v_new):
         if t.dtype != q.dtype:
             raise TypeError("q, kv_pool, k_new, v_new must share one dtype")
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out_like(q, out)
     pool = PagedPool(_dev_ptr(kv_pool, "kv_pool").value, n_blocks, block_size, kv_heads, d,
                      _dtype_code(kv_pool))
     rc = L.kev_paged_attn_decode(_dev_ptr(q, "q"), ctypes.byref(pool), _dev_ptr(block_tables, "block_tables"),
@@ -238,14 +253,12 @@ def _slot_prefill(name, q, k, v, cu_seqlens, kv_pool, slot_ids, prefix_lens, out
     for nm, t in ints[1:]:
         if t.numel() != n_seg:
             raise ValueError(f"{nm} must have one entry per question")
-    if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("out must match q")
+    out = _out_like(q, out)
+    total_tokens = _total_tokens(T, total_tokens)
     pool = KvPool(_dev_ptr(kv_pool, "kv_pool").value, n_slots, capacity, kv_heads, d,
                   _dtype_code(kv_pool))
     args = [_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(cu_seqlens, "cu_seqlens"), n_seg,
-            heads, kv_heads, d, _dev_ptr(out, "out"), T if total_tokens is None else total_tokens,
+            heads, kv_heads, d, _dev_ptr(out, "out"), total_tokens,
             ctypes.byref(pool), _dev_ptr(slot_ids, "slot_ids")]
     if prefix_lens is not None:
         args.append(_dev_ptr(prefix_lens, "prefix_lens"))

@@ -6,6 +6,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -14,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkev.so")
-SOURCES = ["kev_api.hip", "kev_schedule.hip", "kev_prefill_bf16.hip", "kev_prefill_f32.hip",
+SOURCES = ["kev_api.hip", "kev_host.cpp", "kev_schedule.hip", "kev_prefill_bf16.hip", "kev_prefill_f32.hip",
            "kev_decode.hip", "kev_store_kv.hip"]
 ARCH = os.environ.get("KEV_OFFLOAD_ARCH", "gfx950")
 
@@ -34,12 +35,36 @@ def compile_flags() -> list[str]:
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+def scratch_users(remarks: str) -> list[tuple[str, int]]:
+    """Kernels whose compiler resource-usage remarks report private (scratch) memory per lane.
+
+    No kernel of the library may spill: a spill reload inside the prefill loop waits for every
+    outstanding vector-memory operation, including the direct-to-LDS loads in flight, and a
+    register that a spill copies while an inline-asm load is still filling it would be stored
+    before the data lands.
+    """
+    bad, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            bad.append((name, int(m.group(1))))
+    return bad
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + compile_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + compile_flags() + ["-Rpass-analysis=kernel-resource-usage", "-c",
+                                         os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{p.stderr}")
+    bad = scratch_users(p.stderr)
+    if bad:
+        raise RuntimeError(f"{src}: kernels use scratch memory (register spills): {bad}")
     return obj
 
 

@@ -1,4 +1,5 @@
-// kev_api.hip -- the C ABI: argument checks, per-stream workspace, launches.
+// kev_api.hip -- the C ABI: argument checks, stream-ordered workspace, per-stream error words,
+// launches.
 //
 // Everything host-checkable is checked before the first HIP call.  The
 // boundary follows the pages' statement of the problem: the packed stream plus
@@ -11,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -20,6 +22,7 @@
 #include <vector>
 
 #include "../../include/kev.h"
+#include "kev_host.h"
 #include "kev_internal.h"
 
 namespace {
@@ -31,11 +34,16 @@ struct Buffer {
     size_t bytes = 0;
 };
 
+struct DevPool {
+    bool tried = false;
+    hipMemPool_t pool = nullptr;   // null: the device has no stream-ordered allocator
+};
+
 struct State {
     std::mutex mu;
-    std::map<int, int32_t *> err_word;                        // device -> error word
-    std::map<std::pair<int, void *>, Buffer> sched_ws;        // (device, stream)
-    std::map<std::pair<int, void *>, Buffer> decode_ws;       // (device, stream): split states
+    std::map<std::pair<int, void *>, int32_t *> err_word;    // (device, stream) -> error word
+    std::map<int, DevPool> pools;                            // device -> workspace pool
+    std::map<std::pair<int, void *>, Buffer> cached_ws;      // fallback workspace per (device, stream)
 };
 
 State &state() {
@@ -56,18 +64,23 @@ int timed_launch(hipStream_t stream, F f) {
     return KEV_OK;
 }
 
-bool check_enabled() {
-    const char *e = std::getenv("KEV_CHECK");
+bool env_flag(const char *name) {
+    const char *e = std::getenv(name);
     return e && e[0] == '1';
 }
+bool check_enabled() { return env_flag("KEV_CHECK"); }
+bool log_enabled() { return env_flag("KEV_LOG"); }
 
 int to_status(hipError_t e) { return e == hipSuccess ? KEV_OK : KEV_ERR_DEVICE; }
 
-// Device error word of the current device (allocated and zeroed on first use).
-int error_word(int dev, int32_t **out) {
+// Error word of (device, stream): the kernels a call enqueues on `stream` set bits in it, and
+// kev_get_device_errors(stream) reads and clears it, so streams never see each other's flags.
+// Allocated and zeroed on the first call on that stream (kept until the process ends).
+int error_word(int dev, hipStream_t stream, int32_t **out) {
     State &st = state();
     std::lock_guard<std::mutex> lock(st.mu);
-    auto it = st.err_word.find(dev);
+    const auto key = std::make_pair(dev, (void *)stream);
+    auto it = st.err_word.find(key);
     if (it != st.err_word.end()) {
         *out = it->second;
         return KEV_OK;
@@ -75,17 +88,62 @@ int error_word(int dev, int32_t **out) {
     int32_t *p = nullptr;
     if (hipMalloc(&p, 256) != hipSuccess) return KEV_ERR_NO_MEMORY;
     if (hipMemset(p, 0, 256) != hipSuccess) return KEV_ERR_DEVICE;
-    st.err_word[dev] = p;
+    st.err_word[key] = p;
     *out = p;
     return KEV_OK;
 }
 
-// Workspace of at least `bytes` for (device, stream), grown on demand.
-int workspace(std::map<std::pair<int, void *>, Buffer> &m, int dev, hipStream_t stream,
-              size_t bytes, void **out) {
+// Workspace of one call.  Taken stream-ordered from a library-owned pool of the device
+// (hipMallocFromPoolAsync on the caller's stream, returned with hipFreeAsync on the same
+// stream after the call's last kernel): nothing synchronises, concurrent streams never share
+// memory, and the pool keeps its memory between calls (release threshold at the maximum).
+// Devices without a stream-ordered allocator fall back to one cached buffer per (device,
+// stream) that grows on demand; growing it synchronises that stream.
+struct Workspace {
+    void *ptr = nullptr;
+    bool pooled = false;
+};
+
+hipMemPool_t device_pool(int dev) {
     State &st = state();
     std::lock_guard<std::mutex> lock(st.mu);
-    Buffer &b = m[{dev, (void *)stream}];
+    DevPool &dp = st.pools[dev];
+    if (!dp.tried) {
+        dp.tried = true;
+        int ok = 0;
+        if (!std::getenv("KEV_NO_MEMPOOL") &&
+            hipDeviceGetAttribute(&ok, hipDeviceAttributeMemoryPoolsSupported, dev) == hipSuccess && ok) {
+            hipMemPoolProps props;
+            std::memset(&props, 0, sizeof props);
+            props.allocType = hipMemAllocationTypePinned;
+            props.handleTypes = hipMemHandleTypeNone;
+            props.location.type = hipMemLocationTypeDevice;
+            props.location.id = dev;
+            hipMemPool_t pool = nullptr;
+            if (hipMemPoolCreate(&pool, &props) == hipSuccess) {
+                uint64_t keep = UINT64_MAX;
+                if (hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep) == hipSuccess) dp.pool = pool;
+                else hipMemPoolDestroy(pool);
+            }
+        }
+        (void)hipGetLastError();   // a refused attribute or pool is not an error of this call
+    }
+    return dp.pool;
+}
+
+int workspace_acquire(int dev, hipStream_t stream, size_t bytes, Workspace *ws) {
+    bytes = std::max(bytes, (size_t)256);
+    if (hipMemPool_t pool = device_pool(dev)) {
+        if (hipMallocFromPoolAsync(&ws->ptr, bytes, pool, stream) != hipSuccess) {
+            ws->ptr = nullptr;
+            return KEV_ERR_NO_MEMORY;
+        }
+        ws->pooled = true;
+        return KEV_OK;
+    }
+    State &st = state();
+    std::lock_guard<std::mutex> lock(st.mu);
+    Buffer &b = st.cached_ws[{dev, (void *)stream}];
     if (b.bytes < bytes) {
         if (b.ptr) {
             if (hipStreamSynchronize(stream) != hipSuccess) return KEV_ERR_DEVICE;
@@ -93,15 +151,24 @@ int workspace(std::map<std::pair<int, void *>, Buffer> &m, int dev, hipStream_t 
             b.ptr = nullptr;
             b.bytes = 0;
         }
-        size_t want = std::max(bytes, (size_t)1 << 16);
+        const size_t want = std::max(bytes, (size_t)1 << 16);
         if (hipMalloc(&b.ptr, want) != hipSuccess) {
             b.ptr = nullptr;
             return KEV_ERR_NO_MEMORY;
         }
         b.bytes = want;
     }
-    *out = b.ptr;
+    ws->ptr = b.ptr;
+    ws->pooled = false;
     return KEV_OK;
+}
+
+// Returns the workspace once every kernel of the call that uses it has been enqueued.
+int workspace_release(Workspace &ws, hipStream_t stream) {
+    if (!ws.pooled || !ws.ptr) return KEV_OK;
+    const hipError_t e = hipFreeAsync(ws.ptr, stream);
+    ws.ptr = nullptr;
+    return to_status(e);
 }
 
 bool prefill_supported(int32_t head_dim, int32_t dtype) {
@@ -115,13 +182,6 @@ int32_t block_rows_for(int32_t heads, int32_t kv_heads, int32_t dtype) {
     return prefill_shape_bf16(heads, kv_heads).block_rows;
 }
 
-int host_check_seqlens(const int32_t *cu, int32_t n_seg, int32_t total_tokens) {
-    if (cu[0] != 0 || cu[n_seg] != total_tokens) return KEV_ERR_BAD_SEQLENS;
-    for (int32_t s = 0; s < n_seg; ++s)
-        if (cu[s + 1] < cu[s]) return KEV_ERR_BAD_SEQLENS;
-    return KEV_OK;
-}
-
 // Item order of a prefill call: question-major, so concurrently running workgroups share one
 // question's K/V rows in their XCD's L2.  Level-major (longest items first overall) is kept
 // for the schedule entry points; on the Qwen-shaped workloads it timed the same within noise
@@ -133,28 +193,29 @@ int32_t prefill_order(int32_t total_tokens, int32_t head_dim, int32_t dtype) {
     return kOrderQuestion;
 }
 
-// Schedule on the device into the (device, stream) workspace.
-int run_schedule(const int32_t *cu, int32_t n_seg, int32_t total_tokens, int32_t block_rows,
-                 int32_t order, hipStream_t stream, int32_t **ws_out, ScheduleLayout *lay_out,
-                 const int32_t *prefix_lens = nullptr) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
-    int32_t *err = nullptr;
-    int rc = error_word(dev, &err);
-    if (rc) return rc;
-    const int64_t n_max = max_items(total_tokens, n_seg, block_rows);
-    const int64_t hist_len = qblocks(total_tokens, block_rows) + 2;
-    if (hist_len > INT32_MAX || n_max > INT32_MAX / 2) return KEV_ERR_INVALID_ARG;
-    const ScheduleLayout lay = schedule_layout(n_seg, (int32_t)hist_len, n_max);
-    void *ws = nullptr;
-    rc = workspace(state().sched_ws, dev, stream, (size_t)lay.total * sizeof(int32_t), &ws);
-    if (rc) return rc;
-    ScheduleArgs sa{cu, n_seg, total_tokens, block_rows, (int32_t)hist_len, order, n_max,
-                    static_cast<int32_t *>(ws), err, prefix_lens};
-    rc = to_status(launch_schedule(sa, stream));
-    if (rc) return rc;
-    *ws_out = static_cast<int32_t *>(ws);
-    *lay_out = lay;
+// Copies `n` int32 of device memory to the host and waits (KEV_CHECK / KEV_LOG only).
+bool fetch(std::vector<int32_t> &dst, const int32_t *src, size_t n, hipStream_t stream) {
+    dst.resize(n);
+    return n == 0 || (hipMemcpyAsync(dst.data(), src, sizeof(int32_t) * n, hipMemcpyDeviceToHost, stream) ==
+                          hipSuccess &&
+                      hipStreamSynchronize(stream) == hipSuccess);
+}
+
+// Schedule-table geometry of a prefill call.
+struct PrefillPlan {
+    int32_t block_rows, hist_len;
+    int64_t n_max;
+    ScheduleLayout lay;
+};
+
+int plan_prefill(int32_t n_seg, int32_t total_tokens, int32_t heads, int32_t kv_heads, int32_t dtype,
+                 PrefillPlan *pl) {
+    pl->block_rows = block_rows_for(heads, kv_heads, dtype);
+    pl->n_max = max_items(total_tokens, n_seg, pl->block_rows);
+    const int64_t hist_len = qblocks(total_tokens, pl->block_rows) + 2;
+    if (hist_len > INT32_MAX || pl->n_max > INT32_MAX / 2) return KEV_ERR_INVALID_ARG;
+    pl->hist_len = (int32_t)hist_len;
+    pl->lay = schedule_layout(n_seg, pl->hist_len, pl->n_max);
     return KEV_OK;
 }
 
@@ -164,10 +225,10 @@ struct SlotPrefix {
     const int32_t *slot_ids, *prefix_lens;
 };
 
-// Packed prefill; with `pre`, every question is a chunk continuing its slot's cached rows.
-int prefill_impl(const void *q, const void *k, const void *v, const int32_t *cu_seqlens, int32_t n_seg,
-                 int32_t heads, int32_t kv_heads, int32_t head_dim, void *out, int32_t total_tokens,
-                 int32_t dtype, void *stream_, const SlotPrefix *pre) {
+// Host checks of a prefill call (everything that needs no device memory).
+int check_prefill_args(const void *q, const void *k, const void *v, const int32_t *cu_seqlens, int32_t n_seg,
+                       int32_t heads, int32_t kv_heads, int32_t head_dim, const void *out, int32_t total_tokens,
+                       int32_t dtype, const SlotPrefix *pre) {
     if (n_seg < 0 || total_tokens < 0 || heads <= 0 || kv_heads <= 0 || head_dim <= 0)
         return KEV_ERR_INVALID_ARG;
     if (heads % kv_heads != 0) return KEV_ERR_INVALID_ARG;
@@ -177,26 +238,30 @@ int prefill_impl(const void *q, const void *k, const void *v, const int32_t *cu_
     if (n_seg == 0) return total_tokens == 0 ? KEV_OK : KEV_ERR_BAD_SEQLENS;
     if (!cu_seqlens) return KEV_ERR_INVALID_ARG;
     if (total_tokens > 0 && (!q || !k || !v || !out)) return KEV_ERR_INVALID_ARG;
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    return KEV_OK;
+}
 
-    if (check_enabled()) {
-        std::vector<int32_t> h(n_seg + 1);
-        if (hipMemcpyAsync(h.data(), cu_seqlens, sizeof(int32_t) * (n_seg + 1),
-                           hipMemcpyDeviceToHost, stream) != hipSuccess ||
-            hipStreamSynchronize(stream) != hipSuccess)
-            return KEV_ERR_DEVICE;
-        int rc = host_check_seqlens(h.data(), n_seg, total_tokens);
-        if (rc) return rc;
-    }
-    const int32_t br = block_rows_for(heads, kv_heads, dtype);
-    int32_t *ws = nullptr;
-    ScheduleLayout lay;
-    int rc = run_schedule(cu_seqlens, n_seg, total_tokens, br, prefill_order(total_tokens, head_dim, dtype),
-                          stream, &ws, &lay, pre ? pre->prefix_lens : nullptr);
+// Enqueues the work-list pass and the attention kernel of a checked prefill call, with its
+// schedule tables at `ws` (plan.lay.total int32) and its error word at `err`.
+int enqueue_prefill(const void *q, const void *k, const void *v, const int32_t *cu_seqlens, int32_t n_seg,
+                    int32_t heads, int32_t kv_heads, int32_t head_dim, void *out, int32_t total_tokens,
+                    int32_t dtype, const SlotPrefix *pre, const PrefillPlan &pl, int32_t *ws, int32_t *err,
+                    hipStream_t stream) {
+    ScheduleArgs sa{cu_seqlens, n_seg, total_tokens, pl.block_rows, pl.hist_len,
+                    prefill_order(total_tokens, head_dim, dtype), pl.n_max, ws, err,
+                    pre ? pre->prefix_lens : nullptr};
+    int rc = to_status(launch_schedule(sa, stream));
     if (rc) return rc;
+    if (log_enabled()) {
+        std::vector<int32_t> n;
+        if (!fetch(n, ws, 1, stream)) return KEV_ERR_DEVICE;
+        std::fprintf(stderr, "[kev] prefill: %d questions, %d tokens, %d/%d heads, d=%d; %d items of %d rows "
+                             "(capacity %lld), workspace %lld B%s\n",
+                     n_seg, total_tokens, heads, kv_heads, head_dim, n[0], pl.block_rows, (long long)pl.n_max,
+                     (long long)(pl.lay.total * 4), pre ? ", slot prefixes" : "");
+    }
     if (total_tokens == 0) return KEV_OK;   // only empty questions; cu_seqlens still checked
 
-    const int64_t n_max = max_items(total_tokens, n_seg, br);
     PrefillArgs pa{};
     pa.q = q;
     pa.k = k;
@@ -204,24 +269,21 @@ int prefill_impl(const void *q, const void *k, const void *v, const int32_t *cu_
     pa.out = out;
     pa.cu = cu_seqlens;
     pa.sched = ws;
-    pa.items_off = lay.items;
-    pa.rec = ws + lay.rec;
+    pa.items_off = pl.lay.items;
+    pa.rec = ws + pl.lay.rec;
     pa.heads = heads;
     pa.kv_heads = kv_heads;
     pa.group = heads / kv_heads;
     pa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    pa.err = err;
     if (dtype == KEV_BF16) {
         const PrefillShape sh = prefill_shape_bf16(heads, kv_heads);
         pa.row_blocks = sh.row_blocks;
         pa.block_rows = sh.block_rows;
         pa.wg_per_kvh = sh.wg_per_kvh;
-        const int64_t grid = n_max * kv_heads * sh.wg_per_kvh;
+        const int64_t grid = pl.n_max * kv_heads * sh.wg_per_kvh;
         if (grid > INT32_MAX) return KEV_ERR_INVALID_ARG;
         if (pre) {
-            int dev = 0;
-            if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
-            rc = error_word(dev, &pa.err);
-            if (rc) return rc;
             pa.slot_ids = pre->slot_ids;
             pa.prefix_lens = pre->prefix_lens;
             pa.pool = pre->pool->data;
@@ -234,9 +296,46 @@ int prefill_impl(const void *q, const void *k, const void *v, const int32_t *cu_
     pa.row_blocks = 1;
     pa.block_rows = kF32BlockRows;
     pa.n_hgroups = heads;
-    const int64_t grid = n_max * heads;
+    const int64_t grid = pl.n_max * heads;
     if (grid > INT32_MAX) return KEV_ERR_INVALID_ARG;
     return timed_launch(stream, [&] { return launch_prefill_f32(pa, head_dim, grid, stream); });
+}
+
+// KEV_CHECK of cu_seqlens (synchronous).
+int check_seqlens_on_host(const int32_t *cu_seqlens, int32_t n_seg, int32_t total_tokens, hipStream_t stream) {
+    std::vector<int32_t> h;
+    if (!fetch(h, cu_seqlens, (size_t)n_seg + 1, stream)) return KEV_ERR_DEVICE;
+    return host::check_seqlens(h.data(), n_seg, total_tokens);
+}
+
+// Packed prefill; with `pre`, every question is a chunk continuing its slot's cached rows.
+// The schedule tables come from the call's stream-ordered workspace.
+int prefill_impl(const void *q, const void *k, const void *v, const int32_t *cu_seqlens, int32_t n_seg,
+                 int32_t heads, int32_t kv_heads, int32_t head_dim, void *out, int32_t total_tokens,
+                 int32_t dtype, void *stream_, const SlotPrefix *pre) {
+    int rc = check_prefill_args(q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out, total_tokens, dtype,
+                                pre);
+    if (rc || n_seg == 0) return rc;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    if (check_enabled()) {
+        rc = check_seqlens_on_host(cu_seqlens, n_seg, total_tokens, stream);
+        if (rc) return rc;
+    }
+    PrefillPlan pl;
+    rc = plan_prefill(n_seg, total_tokens, heads, kv_heads, dtype, &pl);
+    if (rc) return rc;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
+    int32_t *err = nullptr;
+    rc = error_word(dev, stream, &err);
+    if (rc) return rc;
+    Workspace ws;
+    rc = workspace_acquire(dev, stream, (size_t)pl.lay.total * sizeof(int32_t), &ws);
+    if (rc) return rc;
+    rc = enqueue_prefill(q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out, total_tokens, dtype, pre, pl,
+                         static_cast<int32_t *>(ws.ptr), err, stream);
+    const int rc2 = workspace_release(ws, stream);
+    return rc ? rc : rc2;
 }
 
 // Arguments shared by the two slot-writing prefills: a bf16 pool that matches the K/V heads.
@@ -254,22 +353,14 @@ int check_pool(const kev_kv_pool *pool, int32_t n_seg, int32_t total_tokens, int
 
 // KEV_CHECK: slot ids in range and distinct, and every question's rows (after its prefix,
 // if any) fit the slot.
-int host_check_slots(const kev_kv_pool *pool, const int32_t *slot_ids, const int32_t *prefix_lens,
-                     const int32_t *cu_seqlens, int32_t n_seg, hipStream_t stream) {
-    std::vector<int32_t> ids(n_seg), cu(n_seg + 1), pre(n_seg, 0);
-    if (hipMemcpyAsync(ids.data(), slot_ids, sizeof(int32_t) * n_seg, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-        hipMemcpyAsync(cu.data(), cu_seqlens, sizeof(int32_t) * (n_seg + 1), hipMemcpyDeviceToHost, stream) != hipSuccess ||
-        (prefix_lens && hipMemcpyAsync(pre.data(), prefix_lens, sizeof(int32_t) * n_seg, hipMemcpyDeviceToHost,
-                                       stream) != hipSuccess) ||
-        hipStreamSynchronize(stream) != hipSuccess)
+int check_slots_on_host(const kev_kv_pool *pool, const int32_t *slot_ids, const int32_t *prefix_lens,
+                        const int32_t *cu_seqlens, int32_t n_seg, hipStream_t stream) {
+    std::vector<int32_t> ids, cu, pre;
+    if (!fetch(ids, slot_ids, (size_t)n_seg, stream) || !fetch(cu, cu_seqlens, (size_t)n_seg + 1, stream) ||
+        (prefix_lens && !fetch(pre, prefix_lens, (size_t)n_seg, stream)))
         return KEV_ERR_DEVICE;
-    std::vector<char> seen(pool->n_slots, 0);
-    for (int32_t s = 0; s < n_seg; ++s) {
-        if (ids[s] < 0 || ids[s] >= pool->n_slots || seen[ids[s]]) return KEV_ERR_BAD_SLOT;
-        seen[ids[s]] = 1;
-        if (pre[s] < 0 || (int64_t)pre[s] + cu[s + 1] - cu[s] > pool->capacity) return KEV_ERR_SLOT_OVERFLOW;
-    }
-    return KEV_OK;
+    return host::check_slot_list(ids.data(), prefix_lens ? pre.data() : nullptr, cu.data(), n_seg, pool->n_slots,
+                                 pool->capacity);
 }
 
 // Write every question's K/V rows into its slot, after its prefix rows if any.
@@ -279,7 +370,7 @@ int store_rows(const void *k, const void *v, const int32_t *cu_seqlens, int32_t 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
     int32_t *err = nullptr;
-    int rc = error_word(dev, &err);
+    int rc = error_word(dev, stream, &err);
     if (rc) return rc;
     StoreKvArgs sa{k, v, cu_seqlens, slot_ids, prefix_lens, pool->data, n_seg, total_tokens, kv_heads,
                    pool->n_slots, pool->capacity, err};
@@ -296,42 +387,9 @@ int check_decode_shape(int32_t heads, int32_t kv_heads, int32_t head_dim, int32_
     return KEV_OK;
 }
 
-// KEV_CHECK for a paged decode: cache lengths in range, the block ids a request reads inside
-// the pool, and every append target (block, row) touched by no other request of the call.
-int host_check_paged(const std::vector<int32_t> &tables, const std::vector<int32_t> &lens, int32_t max_blocks,
-                     int32_t n_blocks, int32_t bs) {
-    const int32_t n_req = (int32_t)lens.size();
-    const int64_t limit = std::min<int64_t>(max_blocks, KEV_PAGED_MAX_BLOCKS) * (int64_t)bs;
-    std::vector<char> appended((size_t)n_blocks * bs, 0);
-    for (int32_t r = 0; r < n_req; ++r) {
-        if (lens[r] < 1 || lens[r] > limit) return KEV_ERR_SLOT_OVERFLOW;
-        for (int32_t j = 0; j <= (lens[r] - 1) / bs; ++j) {
-            const int32_t b = tables[(size_t)r * max_blocks + j];
-            if (b < 0 || b >= n_blocks) return KEV_ERR_BAD_SLOT;
-        }
-        const int32_t p = lens[r] - 1;
-        char &a = appended[(size_t)tables[(size_t)r * max_blocks + p / bs] * bs + p % bs];
-        if (a) return KEV_ERR_BAD_SLOT;
-        a = 1;
-    }
-    for (int32_t r = 0; r < n_req; ++r)
-        for (int32_t p = 0; p + 1 < lens[r]; ++p)
-            if (appended[(size_t)tables[(size_t)r * max_blocks + p / bs] * bs + p % bs]) return KEV_ERR_BAD_SLOT;
-    return KEV_OK;
-}
-
-// Workgroups per decode unit (request, KV head).  With fewer units than the CUs hold at once
-// (two workgroups each), one workgroup per unit leaves CUs idle and each unit's time is the
-// latency of a few sequential tile loads, so its tiles are split: about two workgroups per CU
-// in total, at most 8 per unit (more splits cost more in the merge than they save; measured
-// on the 64-request decode workload cut to 1..32 requests).  KEV_DECODE_SPLITS=N forces N.
-int decode_splits(int64_t units, int cus) {
-    if (const char *e = std::getenv("KEV_DECODE_SPLITS")) {
-        const int n = std::atoi(e);
-        if (n >= 1) return std::min(n, kMaxDecodeSplits);
-    }
-    if (units >= (int64_t)cus) return 1;
-    return (int)std::min<int64_t>(8, (2 * (int64_t)cus + units - 1) / units);
+int forced_splits() {
+    const char *e = std::getenv("KEV_DECODE_SPLITS");
+    return e ? std::atoi(e) : 0;
 }
 
 // Launch a decode (slot or paged pool) once the pool-specific fields of `da` are set.
@@ -340,7 +398,7 @@ int run_decode(DecodeArgs &da, const void *q, void *data, int32_t kv_heads, int3
                int32_t heads, bool paged, hipStream_t stream) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
-    int rc = error_word(dev, &da.err);
+    int rc = error_word(dev, stream, &da.err);
     if (rc) return rc;
     da.q = q;
     da.pool = data;
@@ -357,15 +415,8 @@ int run_decode(DecodeArgs &da, const void *q, void *data, int32_t kv_heads, int3
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         return KEV_ERR_DEVICE;
-    da.n_split = decode_splits(units, cus);
+    da.n_split = host::decode_splits(units, cus, forced_splits());
     if (units * da.n_split > INT32_MAX) return KEV_ERR_INVALID_ARG;
-    if (da.n_split > 1) {
-        void *ws = nullptr;
-        const size_t bytes = (size_t)units * da.n_split * da.group * (head_dim + 2) * sizeof(float);
-        rc = workspace(state().decode_ws, dev, stream, bytes, &ws);
-        if (rc) return rc;
-        da.part = static_cast<float *>(ws);
-    }
     // Unit order (requests ranked by length inside the kernel, at most 64 requests): longest
     // first when the grid does not fit the CUs at once (two workgroups each); when it fits but
     // some CUs hold two workgroups, a long and a short unit share each such CU (measured on the
@@ -376,7 +427,22 @@ int run_decode(DecodeArgs &da, const void *q, void *data, int32_t kv_heads, int3
         if (units > 2 * (int64_t)cus) da.ranked = 1;
         else if (units > cus) da.ranked = 2;
     }
-    return timed_launch(stream, [&] { return launch_decode_bf16(da, head_dim, paged, stream); });
+    const size_t part_bytes =
+        da.n_split > 1 ? (size_t)units * da.n_split * da.group * (head_dim + 2) * sizeof(float) : 0;
+    if (log_enabled())
+        std::fprintf(stderr, "[kev] %s decode: %d requests, %d/%d heads, d=%d; %lld units x %d splits, "
+                             "order %d, workspace %zu B\n",
+                     paged ? "paged" : "slot", n_req, heads, kv_heads, head_dim, (long long)units, da.n_split,
+                     da.ranked, part_bytes);
+    Workspace ws;
+    if (da.n_split > 1) {
+        rc = workspace_acquire(dev, stream, part_bytes, &ws);
+        if (rc) return rc;
+        da.part = static_cast<float *>(ws.ptr);
+    }
+    rc = timed_launch(stream, [&] { return launch_decode_bf16(da, head_dim, paged, stream); });
+    const int rc2 = workspace_release(ws, stream);
+    return rc ? rc : rc2;
 }
 
 }  // namespace
@@ -419,7 +485,7 @@ int kev_packed_attn_prefill_slots(const void *q, const void *k, const void *v,
     if (rc) return rc;
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     if (check_enabled() && n_seg > 0) {
-        rc = host_check_slots(pool, slot_ids, nullptr, cu_seqlens, n_seg, stream);
+        rc = check_slots_on_host(pool, slot_ids, nullptr, cu_seqlens, n_seg, stream);
         if (rc) return rc;
     }
     rc = prefill_impl(q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out, total_tokens, KEV_BF16,
@@ -438,7 +504,7 @@ int kev_chunked_prefill_slots(const void *q, const void *k, const void *v, const
     if (n_seg > 0 && !prefix_lens) return KEV_ERR_INVALID_ARG;
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     if (check_enabled() && n_seg > 0) {
-        rc = host_check_slots(pool, slot_ids, prefix_lens, cu_seqlens, n_seg, stream);
+        rc = check_slots_on_host(pool, slot_ids, prefix_lens, cu_seqlens, n_seg, stream);
         if (rc) return rc;
     }
     const SlotPrefix pre{pool, slot_ids, prefix_lens};
@@ -464,17 +530,11 @@ int kev_slot_attn_decode(const void *q, const kev_kv_pool *pool, const int32_t *
     hipStream_t stream = static_cast<hipStream_t>(stream_);
 
     if (check_enabled()) {
-        std::vector<int32_t> ids(n_req), lens(n_req);
-        if (hipMemcpyAsync(ids.data(), slot_ids, sizeof(int32_t) * n_req, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-            hipMemcpyAsync(lens.data(), cache_lens, sizeof(int32_t) * n_req, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-            hipStreamSynchronize(stream) != hipSuccess)
+        std::vector<int32_t> ids, lens;
+        if (!fetch(ids, slot_ids, (size_t)n_req, stream) || !fetch(lens, cache_lens, (size_t)n_req, stream))
             return KEV_ERR_DEVICE;
-        std::vector<char> seen(pool->n_slots, 0);
-        for (int32_t r = 0; r < n_req; ++r) {
-            if (ids[r] < 0 || ids[r] >= pool->n_slots || seen[ids[r]]) return KEV_ERR_BAD_SLOT;
-            seen[ids[r]] = 1;
-            if (lens[r] < 1 || lens[r] > pool->capacity) return KEV_ERR_SLOT_OVERFLOW;
-        }
+        rc = host::check_decode(ids.data(), lens.data(), n_req, pool->n_slots, pool->capacity);
+        if (rc) return rc;
     }
     DecodeArgs da{};
     da.slot_ids = slot_ids;
@@ -499,13 +559,11 @@ int kev_paged_attn_decode(const void *q, const kev_paged_pool *pool, const int32
     hipStream_t stream = static_cast<hipStream_t>(stream_);
 
     if (check_enabled()) {
-        std::vector<int32_t> tables((size_t)n_req * max_blocks), lens(n_req);
-        if (hipMemcpyAsync(tables.data(), block_tables, sizeof(int32_t) * tables.size(), hipMemcpyDeviceToHost,
-                           stream) != hipSuccess ||
-            hipMemcpyAsync(lens.data(), cache_lens, sizeof(int32_t) * n_req, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-            hipStreamSynchronize(stream) != hipSuccess)
+        std::vector<int32_t> tables, lens;
+        if (!fetch(tables, block_tables, (size_t)n_req * max_blocks, stream) ||
+            !fetch(lens, cache_lens, (size_t)n_req, stream))
             return KEV_ERR_DEVICE;
-        rc = host_check_paged(tables, lens, max_blocks, pool->n_blocks, bs);
+        rc = host::check_paged(tables.data(), lens.data(), n_req, max_blocks, pool->n_blocks, bs);
         if (rc) return rc;
     }
     DecodeArgs da{};
@@ -531,13 +589,14 @@ int kev_get_device_errors(void *stream_, int32_t *flags_out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
     int32_t *err = nullptr;
-    int rc = error_word(dev, &err);
+    int rc = error_word(dev, stream, &err);
     if (rc) return rc;
-    if (hipStreamSynchronize(stream) != hipSuccess) return KEV_ERR_DEVICE;
     int32_t v = 0;
-    if (hipMemcpy(&v, err, sizeof v, hipMemcpyDeviceToHost) != hipSuccess) return KEV_ERR_DEVICE;
-    if (hipMemset(err, 0, sizeof v) != hipSuccess) return KEV_ERR_DEVICE;
-    if (hipDeviceSynchronize() != hipSuccess) return KEV_ERR_DEVICE;
+    // Stream order: the read follows every kernel enqueued on this stream before the call, and
+    // the clear follows the read.
+    if (hipMemcpyAsync(&v, err, sizeof v, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipMemsetAsync(err, 0, sizeof v, stream) != hipSuccess || hipStreamSynchronize(stream) != hipSuccess)
+        return KEV_ERR_DEVICE;
     *flags_out = v;
     return KEV_OK;
 }
@@ -548,43 +607,7 @@ int kev_prefill_order(int32_t total_tokens, int32_t head_dim, int32_t dtype) {
 
 int kev_schedule_host(const int32_t *cu, int32_t n_seg, int32_t block_rows, int32_t order,
                       int32_t *items_out, int32_t max_items_, int32_t *n_items_out) {
-    if (!cu || n_seg < 0 || block_rows <= 0 || !n_items_out) return KEV_ERR_INVALID_ARG;
-    if (order != kOrderQuestion && order != kOrderLevel) return KEV_ERR_INVALID_ARG;
-    if (n_seg == 0) {
-        *n_items_out = 0;
-        return KEV_OK;
-    }
-    int rc = host_check_seqlens(cu, n_seg, cu[n_seg]);
-    if (rc) return rc;
-    std::vector<int32_t> nb(n_seg), qs(n_seg);   // qs: questions by descending block count
-    int64_t total = 0;
-    for (int32_t s = 0; s < n_seg; ++s) {
-        nb[s] = qblocks(cu[s + 1] - cu[s], block_rows);
-        total += nb[s];
-        qs[s] = s;
-    }
-    if (total > max_items_ || (total > 0 && !items_out)) return KEV_ERR_INVALID_ARG;
-    std::stable_sort(qs.begin(), qs.end(), [&](int32_t x, int32_t y) { return nb[x] > nb[y]; });
-    int64_t p = 0;
-    if (order == kOrderLevel) {
-        int32_t maxnb = 0;
-        for (int32_t s = 0; s < n_seg; ++s) maxnb = std::max(maxnb, nb[s]);
-        for (int32_t t = maxnb - 1; t >= 0; --t)
-            for (int32_t i = 0; i < n_seg && nb[qs[i]] > t; ++i) {
-                items_out[2 * p] = qs[i];
-                items_out[2 * p + 1] = t;
-                ++p;
-            }
-    } else {
-        for (int32_t i = 0; i < n_seg; ++i)
-            for (int32_t t = nb[qs[i]] - 1; t >= 0; --t) {
-                items_out[2 * p] = qs[i];
-                items_out[2 * p + 1] = t;
-                ++p;
-            }
-    }
-    *n_items_out = (int32_t)p;
-    return KEV_OK;
+    return host::schedule(cu, n_seg, block_rows, order, items_out, max_items_, n_items_out);
 }
 
 int kev_schedule_device(const int32_t *cu_seqlens, int32_t n_seg, int32_t total_tokens,
@@ -594,20 +617,30 @@ int kev_schedule_device(const int32_t *cu_seqlens, int32_t n_seg, int32_t total_
         return KEV_ERR_INVALID_ARG;
     if (order != kOrderQuestion && order != kOrderLevel) return KEV_ERR_INVALID_ARG;
     hipStream_t stream = static_cast<hipStream_t>(stream_);
-    int32_t *ws = nullptr;
-    ScheduleLayout lay;
-    int rc = run_schedule(cu_seqlens, n_seg, total_tokens, block_rows, order, stream, &ws, &lay);
+    const int64_t n_max = max_items(total_tokens, n_seg, block_rows);
+    const int64_t hist_len = qblocks(total_tokens, block_rows) + 2;
+    if (hist_len > INT32_MAX || n_max > INT32_MAX / 2) return KEV_ERR_INVALID_ARG;
+    const ScheduleLayout lay = schedule_layout(n_seg, (int32_t)hist_len, n_max);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
+    int32_t *err = nullptr;
+    int rc = error_word(dev, stream, &err);
     if (rc) return rc;
-    int32_t n = 0;
-    if (hipMemcpyAsync(&n, ws, sizeof n, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-        hipStreamSynchronize(stream) != hipSuccess)
-        return KEV_ERR_DEVICE;
-    if (n > max_items_ || (n > 0 && !items_out)) return KEV_ERR_INVALID_ARG;
-    if (n > 0 && (hipMemcpyAsync(items_out, ws + lay.items, sizeof(int32_t) * 2 * n,
-                                 hipMemcpyDeviceToHost, stream) != hipSuccess ||
-                  hipStreamSynchronize(stream) != hipSuccess))
-        return KEV_ERR_DEVICE;
-    *n_items_out = n;
+    Workspace ws;
+    rc = workspace_acquire(dev, stream, (size_t)lay.total * sizeof(int32_t), &ws);
+    if (rc) return rc;
+    int32_t *w = static_cast<int32_t *>(ws.ptr);
+    ScheduleArgs sa{cu_seqlens, n_seg, total_tokens, block_rows, (int32_t)hist_len, order, n_max, w, err, nullptr};
+    rc = to_status(launch_schedule(sa, stream));
+    std::vector<int32_t> n, items;
+    if (!rc && !fetch(n, w, 1, stream)) rc = KEV_ERR_DEVICE;
+    if (!rc && (n[0] > max_items_ || (n[0] > 0 && !items_out))) rc = KEV_ERR_INVALID_ARG;
+    if (!rc && !fetch(items, w + lay.items, 2 * (size_t)n[0], stream)) rc = KEV_ERR_DEVICE;
+    const int rc2 = workspace_release(ws, stream);
+    if (rc) return rc;
+    if (rc2) return rc2;
+    std::copy(items.begin(), items.end(), items_out);
+    *n_items_out = n[0];
     return KEV_OK;
 }
 

@@ -78,7 +78,7 @@ __device__ __forceinline__ void dma16(const void *g, unsigned lds_addr) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(g), "s"(m0v)
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // Same load with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset
@@ -92,7 +92,7 @@ __device__ __forceinline__ void dma16s(const void *base, unsigned voff, unsigned
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(voff), "s"(sb), "s"(m0v)
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // Per-lane part of a direct load of tile rows [r0, r0 + RPI): the row this lane fills and

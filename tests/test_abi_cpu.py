@@ -226,3 +226,37 @@ def test_kernel_events_hook_arguments(lib):
     assert lib.kev_set_kernel_events(p, None) == K.KEV_ERR_INVALID_ARG
     assert lib.kev_set_kernel_events(None, p) == K.KEV_ERR_INVALID_ARG
     assert lib.kev_set_kernel_events(None, None) == K.KEV_OK
+
+
+def test_binding_checks_out_and_total_tokens_before_any_device_call():
+    """The kernels write q.shape elements through `out` and touch rows up to total_tokens, which
+    the C ABI cannot check: the binding rejects a mismatched `out` or an out-of-range
+    total_tokens before it takes a device pointer (CPU tensors reach the check and fail there)."""
+    import torch
+    q = torch.zeros(10, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(10, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4, 10], dtype=torch.int32)
+    with pytest.raises(ValueError, match="out must be"):
+        K.kev_packed_attn_prefill(q, k, k, cu, out=torch.zeros(10, 4, 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out must be"):
+        K.kev_packed_attn_prefill(q, k, k, cu, out=torch.zeros(10, 4, 64, dtype=torch.float32))
+    for bad in (11, -1):
+        with pytest.raises(ValueError, match="total_tokens"):
+            K.kev_packed_attn_prefill(q, k, k, cu, total_tokens=bad)
+    pool = torch.zeros(3, 2, 2, 16, 64, dtype=torch.bfloat16)
+    ids = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="total_tokens"):
+        K.kev_packed_attn_prefill_slots(q, k, k, cu, pool, ids, total_tokens=12)
+    with pytest.raises(ValueError, match="out must be"):
+        K.kev_chunked_prefill_slots(q, k, k, cu, pool, ids, ids, out=torch.zeros(9, 4, 64, dtype=torch.bfloat16))
+
+    dq = torch.zeros(2, 4, 64, dtype=torch.bfloat16)
+    kn = torch.zeros(2, 2, 64, dtype=torch.bfloat16)
+    lens = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="out must be"):
+        K.kev_slot_attn_decode(dq, pool, ids, lens, kn, kn, out=torch.zeros(1, 4, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out must be"):
+        K.kev_slot_attn_decode(dq, pool, ids, lens, kn, kn, out=torch.zeros(2, 4, 64, dtype=torch.float16))
+    tables = torch.zeros(2, 1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="out must be"):
+        K.kev_paged_attn_decode(dq, pool, tables, lens, kn, kn, out=torch.zeros(2, 4, 63, dtype=torch.bfloat16))

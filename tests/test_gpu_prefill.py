@@ -56,6 +56,12 @@ def test_qwen3_shape_full_size_sampled(orc):
     assert_parity(got[rows, heads], ref, case.dtype, "qwen3-8b full size, sampled rows")
 
 
+def test_skewed_long_reduced_heads_every_row(orc):
+    # the same 256 lengths (131072 tokens, questions up to 6967 rows: up to 218 key tiles per
+    # query block), 8 q / 2 kv heads: every output element against the oracle
+    check_full(W.prefill_case("skewed_long", heads=8, kv_heads=2), orc, "skewed long lengths, 8/2 heads")
+
+
 def test_skewed_long_sampled(orc):
     case = W.prefill_case("skewed_long")
     say(f"prefill skewed long T={case.total_tokens}")
