@@ -33,10 +33,15 @@
 //   S^T[key][q] = K_tile[key][:] . Q^T[:][q]     A = K from LDS, B = Q in VGPRs
 //   O^T[d][q]  += V^T[d][key]   . P^T[key][q]    A = V^T from LDS, B = P^T in VGPRs
 // With the query index on the lane (n = lane % 32), each lane owns one query
-// row: row max and row sum need one exchange between the two half-waves, the
-// rescale of O^T is lane-uniform, and P^T feeds the second MFMA straight from
-// the first one's accumulators (converted to bf16).  Staging and operand reads
-// are described in kev_mfma_core.h.
+// row: a row max needs one exchange between the two half-waves, the rescale of
+// O^T is lane-uniform, and P^T feeds the second MFMA straight from the first
+// one's accumulators (converted to bf16).  Staging and operand reads are
+// described in kev_mfma_core.h.
+//
+// Softmax.  The weights of a tile are taken against the running max as it
+// stands and the max only moves when a lane's tile sum leaves a fixed bound
+// (tile_pv below), so the common tile spends one FMA and one exp per score, a
+// bf16 conversion per pair and a dot product per pair for the row sum.
 //
 // Pipeline.  Tiles are 32 keys.  K and V each have four LDS stages and direct
 // loads run three tiles ahead.  Iteration j starts with the scores of tile j
@@ -178,47 +183,60 @@ struct TileLoader {
 };
 
 // Online-softmax state of one lane (one query row; the lane pair l, l^32 shares it).
-// The running max is only moved (and O^T, l rescaled) when a new score exceeds it by more
-// than kLazy (log2 units); otherwise weights are taken against the stale max, so they stay
-// below 2^kLazy.  Either way out = O / l is the same softmax average.
 template <int D>
 struct RowState {
     f32x16 o[D / 32];
-    float m, l, alpha;
-    bool pending;   // O^T still has to be multiplied by alpha
+    float m, l;
 };
 
-// Row max of a scored (and, where needed, masked) 32-key tile and the lazy update of the
-// running max; l is rescaled here, O^T by apply_rescale before the next P.V product.
-template <int D>
-__device__ __forceinline__ void tile_max(const f32x16 &s, float c, RowState<D> &st) {
-    float mx = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int i = 2; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
-    mx = max_halves_valu(mx) * c;
-    st.pending = __any(mx > st.m + kLazy);
-    if (st.pending) {
-        const float m_new = fmaxf(st.m, mx);
-        st.alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-        st.m = m_new;
-        st.l *= st.alpha;
-    }
-}
+// Weights of a tile are taken against the running max m as it stands.  A lane's sum of its 16
+// weights bounds each of them; only when that sum exceeds 2^15, or is not finite (the first
+// tile, where m is still -inf), is m moved to the tile's max and O^T, l rescaled (rare after
+// the first tile: the max has to grow by about 11 in log2 units).  Either way out = O / l is
+// the same softmax average; the per-tile row max and its half-wave exchange leave the common
+// path.
+constexpr float kGuardSum = 32768.f;
 
-// P = exp2(S*c - m) in bf16 (two 16-key chunks) with the row sums in fp32.
-template <int D>
-__device__ __forceinline__ void tile_p(const f32x16 &s, float c, RowState<D> &st, bf16x8 *pb) {
-    const float mneg = -st.m;
-    float part[2];
+// P = exp2(S*c - m) in bf16 (two 16-key chunks, the B operand of P.V) and this lane's sum of
+// the 16 weights, taken from the bf16 values with v_dot2_f32_bf16 against (1, 1), so the row
+// sum holds exactly the weights P.V uses.  (Inline asm: the compiler's builtin for this
+// instruction, fed from a bit-cast vector, was seen to read the first pair for all four.)
+__device__ __forceinline__ float tile_p(const f32x16 &s, float c, float mneg, bf16x8 *pb) {
+    const unsigned one2 = 0x3F803F80u;   // bf16 (1, 1)
+    float acc = 0.f;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
         f32x8 e;
 #pragma unroll
         for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s[cc * 8 + i], c, mneg));
-        part[cc] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
         pb[cc] = __builtin_convertvector(e, bf16x8);
+        const u32x4 w = __builtin_bit_cast(u32x4, pb[cc]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm("v_dot2_f32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(w[i]), "v"(one2));
     }
-    st.l += part[0] + part[1];
+    return acc;
+}
+
+// Moves the running max of the rows that need it (`need`: the row's tile sum left the bound in
+// either half-wave) to the max of the scored tile, and rescales their O^T and l.  Other rows
+// keep their max (alpha = 1, exact), so their weights come out bit for bit as without the
+// move: what a row computes never depends on another row's scores, and in particular not on
+// keys past its diagonal that a later row of the same wavefront sees.
+template <int D>
+__device__ __forceinline__ void move_max(const f32x16 &s, float c, bool need, RowState<D> &st) {
+    float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
+    mx = max_halves_valu(mx) * c;
+    const bool row_need = max_halves_valu(need ? 1.f : 0.f) > 0.f;
+    const float m_new = row_need ? fmaxf(st.m, mx) : st.m;
+    const float alpha = row_need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
+    st.m = m_new;
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.o[db][i] *= alpha;
 }
 
 // O^T += V^T P^T with the V^T fragments of the tile in registers (vf[cc * DB + db]:
@@ -233,22 +251,18 @@ __device__ __forceinline__ void tile_o(const bf16x8 *pb, const bf16x8 *vf, RowSt
             st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cc * DB + db], pb[cc], st.o[db], 0, 0, 0);
 }
 
+// Softmax of a scored (and, where needed, masked) tile and its P.V product.
 template <int D>
 __device__ __forceinline__ void tile_pv(const f32x16 &s, const bf16x8 *vf, float c, RowState<D> &st) {
     bf16x8 pb[2];
-    tile_p<D>(s, c, st, pb);
-    tile_o<D>(pb, vf, st);
-}
-
-template <int D>
-__device__ __forceinline__ void apply_rescale(RowState<D> &st) {
-    if (st.pending) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) st.o[db][i] *= st.alpha;
-        st.pending = false;
+    float lt = tile_p(s, c, -st.m, pb);
+    const bool need = !(lt <= kGuardSum);
+    if (__any(need)) {   // wave-uniform branch; the move itself is per row
+        move_max<D>(s, c, need, st);
+        lt = tile_p(s, c, -st.m, pb);
     }
+    st.l += lt;
+    tile_o<D>(pb, vf, st);
 }
 
 // Causal / question-end select on a 32-key tile that crosses the diagonal or the end.
@@ -331,8 +345,6 @@ void prefill_bf16_kernel(PrefillArgs p) {
         for (int i = 0; i < 16; ++i) st.o[db][i] = 0.f;
     st.m = -INFINITY;
     st.l = 0.f;
-    st.alpha = 1.f;
-    st.pending = false;
     const float c = p.scale_log2;
 
     TileLoader<D, NWAVE, PREFIX> ld;
@@ -409,8 +421,6 @@ void prefill_bf16_kernel(PrefillArgs p) {
 #pragma unroll
             for (int dc = 0; dc < C::DC; ++dc) kf[dc] = k_frag<D>(kn, dc);
             if (j >= n_full) mask_tile<D>(s, j * KT, P + qrow, P + L);
-            tile_max<D>(s, c, st);
-            apply_rescale<D>(st);
             tile_pv<D>(s, vf, c, st);
             if (j + 1 < my_tiles) s = score();
         }
