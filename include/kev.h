@@ -81,7 +81,8 @@ typedef enum {
     KEV_ERR_SLOT_OVERFLOW = -4, /* a cache length outside [1, capacity] */
     KEV_ERR_BAD_SLOT = -5,      /* a slot id outside [0, n_slots), or repeated within one call */
     KEV_ERR_DEVICE = -6,        /* a HIP call failed */
-    KEV_ERR_NO_MEMORY = -7      /* workspace allocation failed */
+    KEV_ERR_NO_MEMORY = -7,     /* workspace allocation failed */
+    KEV_ERR_SCRATCH_LIMIT = -8  /* kev_packed_attn_prefill_noalloc: work list exceeds its scratch */
 } kev_status;
 
 /* Bits of the per-stream error word (kev_get_device_errors). */
@@ -114,6 +115,29 @@ int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
                             const int32_t *cu_seqlens, int32_t n_seg,
                             int32_t heads, int32_t kv_heads, int32_t head_dim,
                             void *out, int32_t total_tokens, int32_t dtype, void *stream);
+
+/*
+ * kev_packed_attn_prefill without any allocation, for callers that cannot
+ * allocate device memory during the call: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, checks,
+ * kernels and results as kev_packed_attn_prefill (bitwise); it calls no
+ * hipMalloc, hipFree or allocating library routine.
+ *
+ * Its work list and its error word live in a device array of 4 MiB that the
+ * library holds on every GPU it runs on until the process ends.  A call whose
+ * work list needs more (about 3.5 M tokens at the 32-row blocks of the 32/8-head
+ * shape, fewer with more questions) returns KEV_ERR_SCRATCH_LIMIT and enqueues
+ * nothing.  Every call on one GPU shares that array, and a call overwrites what
+ * the previous one left there: calls that overlap on one GPU (on different
+ * streams, or from different host threads without ordering) race and are not
+ * allowed.  Device-array errors set bits in the array's own error word, which
+ * the next kev_get_device_errors on that GPU (any stream) reports and clears.
+ * KEV_CHECK and KEV_LOG are ignored (both would copy to the host and wait).
+ */
+int kev_packed_attn_prefill_noalloc(const void *q, const void *k, const void *v,
+                                    const int32_t *cu_seqlens, int32_t n_seg,
+                                    int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                    void *out, int32_t total_tokens, int32_t dtype, void *stream);
 
 /*
  * KV slot pool geometry.  `data` is a caller-owned device buffer laid out as
@@ -290,7 +314,9 @@ const char *kev_status_string(int status);
  * *flags_out (a KEV_DEVERR_* bitmask, 0 if every unit of every call enqueued
  * on `stream` since the last read was valid), after all work enqueued on
  * `stream` before this call; returns once the read is done (synchronises
- * `stream`).  Flags raised by calls on other streams are not seen here.
+ * `stream`).  Flags raised by calls on other streams are not seen here, except
+ * those of kev_packed_attn_prefill_noalloc, whose one error word per device is
+ * read and cleared too.
  */
 int kev_get_device_errors(void *stream, int32_t *flags_out);
 

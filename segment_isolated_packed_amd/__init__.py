@@ -23,6 +23,7 @@ KEV_ERR_SLOT_OVERFLOW = -4
 KEV_ERR_BAD_SLOT = -5
 KEV_ERR_DEVICE = -6
 KEV_ERR_NO_MEMORY = -7
+KEV_ERR_SCRATCH_LIMIT = -8
 KEV_DEVERR_SEQLENS, KEV_DEVERR_SLOT, KEV_DEVERR_CACHE_LEN, KEV_DEVERR_BLOCK = 1, 2, 4, 8
 KEV_PAGED_MAX_BLOCKS = 2048
 KEV_ORDER_QUESTION, KEV_ORDER_LEVEL = 0, 1
@@ -65,6 +66,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L = ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
     P, I = ctypes.c_void_p, ctypes.c_int32
     L.kev_packed_attn_prefill.argtypes = [P, P, P, P, I, I, I, I, P, I, I, P]
+    L.kev_packed_attn_prefill_noalloc.argtypes = [P, P, P, P, I, I, I, I, P, I, I, P]
     L.kev_slot_attn_decode.argtypes = [P, ctypes.POINTER(KvPool), P, P, P, P, P, I, I, P]
     L.kev_packed_attn_prefill_slots.argtypes = [P, P, P, P, I, I, I, I, P, I, ctypes.POINTER(KvPool), P, P]
     L.kev_chunked_prefill_slots.argtypes = [P, P, P, P, I, I, I, I, P, I, ctypes.POINTER(KvPool), P, P, P]
@@ -77,7 +79,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kev_prefill_order.argtypes = [I, I, I]
     L.kev_schedule_host.argtypes = [P, I, I, I, P, I, ctypes.POINTER(I)]
     L.kev_schedule_device.argtypes = [P, I, I, I, I, P, I, ctypes.POINTER(I), P]
-    for f in (L.kev_packed_attn_prefill, L.kev_slot_attn_decode, L.kev_packed_attn_prefill_slots,
+    for f in (L.kev_packed_attn_prefill, L.kev_packed_attn_prefill_noalloc, L.kev_slot_attn_decode, L.kev_packed_attn_prefill_slots,
               L.kev_chunked_prefill_slots, L.kev_paged_attn_decode, L.kev_get_device_errors,
               L.kev_set_kernel_events,
               L.kev_prefill_block_rows, L.kev_prefill_order, L.kev_schedule_host,
@@ -163,6 +165,32 @@ def kev_packed_attn_prefill(q, k, v, cu_seqlens, out=None, total_tokens: int | N
                                    heads, kv_heads, d, _dev_ptr(out, "out"), total_tokens,
                                    _dtype_code(q), _stream(stream))
     _check(rc, "kev_packed_attn_prefill")
+    return out
+
+
+def kev_packed_attn_prefill_noalloc(q, k, v, cu_seqlens, out, total_tokens: int | None = None, stream=None):
+    """kev_packed_attn_prefill with no allocation: the work list lives in the library's
+    per-GPU device scratch (4 MiB), and `out` must be given (nothing is allocated here
+    either).  Calls that overlap on one GPU race on that scratch."""
+    import torch
+    L = load_library()
+    T, heads, d = q.shape
+    kv_heads = k.shape[1]
+    if k.shape != (T, kv_heads, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [T, kv_heads, head_dim] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if out is None:
+        raise ValueError("out is required (this entry point allocates nothing)")
+    out = _out_like(q, out)
+    total_tokens = _total_tokens(T, total_tokens)
+    rc = L.kev_packed_attn_prefill_noalloc(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                           _dev_ptr(cu_seqlens, "cu_seqlens"), cu_seqlens.numel() - 1,
+                                           heads, kv_heads, d, _dev_ptr(out, "out"), total_tokens,
+                                           _dtype_code(q), _stream(stream))
+    _check(rc, "kev_packed_attn_prefill_noalloc")
     return out
 
 

@@ -44,11 +44,36 @@ struct State {
     std::map<std::pair<int, void *>, int32_t *> err_word;    // (device, stream) -> error word
     std::map<int, DevPool> pools;                            // device -> workspace pool
     std::map<std::pair<int, void *>, Buffer> cached_ws;      // fallback workspace per (device, stream)
+    std::map<int, int32_t *> scratch_ptr;                    // device -> address of `scratch`
 };
 
 State &state() {
     static State *s = new State();   // never destroyed: outlives static teardown order
     return *s;
+}
+
+// Scratch of the no-allocation prefill (kev_packed_attn_prefill_noalloc): a file-scope device
+// array, one copy per GPU, held until the process ends.  Word 0 is that entry point's error
+// word; its work-list tables start 256 bytes in.  In host code `scratch` only names the
+// symbol: its device address on each GPU comes from hipGetSymbolAddress (scratch_on).
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+constexpr size_t kScratchTables = 256;   // bytes before the tables (the error word lives there)
+static __device__ __align__(256) int32_t scratch[kScratchBytes / sizeof(int32_t)];
+
+// Device address of `scratch` on device `dev` (looked up once per device, with it current).
+int scratch_on(int dev, int32_t **out) {
+    State &st = state();
+    std::lock_guard<std::mutex> lock(st.mu);
+    auto it = st.scratch_ptr.find(dev);
+    if (it != st.scratch_ptr.end()) {
+        *out = it->second;
+        return KEV_OK;
+    }
+    int32_t *ptr = nullptr;
+    if (hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KEV_ERR_DEVICE;
+    st.scratch_ptr[dev] = ptr;
+    *out = ptr;
+    return KEV_OK;
 }
 
 // Events the calls of this host thread record around their main kernel (kev_set_kernel_events).
@@ -246,13 +271,13 @@ int check_prefill_args(const void *q, const void *k, const void *v, const int32_
 int enqueue_prefill(const void *q, const void *k, const void *v, const int32_t *cu_seqlens, int32_t n_seg,
                     int32_t heads, int32_t kv_heads, int32_t head_dim, void *out, int32_t total_tokens,
                     int32_t dtype, const SlotPrefix *pre, const PrefillPlan &pl, int32_t *ws, int32_t *err,
-                    hipStream_t stream) {
+                    hipStream_t stream, bool may_log = true) {
     ScheduleArgs sa{cu_seqlens, n_seg, total_tokens, pl.block_rows, pl.hist_len,
                     prefill_order(total_tokens, head_dim, dtype), pl.n_max, ws, err,
                     pre ? pre->prefix_lens : nullptr};
     int rc = to_status(launch_schedule(sa, stream));
     if (rc) return rc;
-    if (log_enabled()) {
+    if (may_log && log_enabled()) {
         std::vector<int32_t> n;
         if (!fetch(n, ws, 1, stream)) return KEV_ERR_DEVICE;
         std::fprintf(stderr, "[kev] prefill: %d questions, %d tokens, %d/%d heads, d=%d; %d items of %d rows "
@@ -459,6 +484,7 @@ const char *kev_status_string(int status) {
     case KEV_ERR_BAD_SLOT: return "slot or block id out of range, or repeated";
     case KEV_ERR_DEVICE: return "HIP runtime error";
     case KEV_ERR_NO_MEMORY: return "workspace allocation failed";
+    case KEV_ERR_SCRATCH_LIMIT: return "work list larger than the no-allocation prefill's 4 MiB device scratch";
     default: return "unknown status";
     }
 }
@@ -475,6 +501,27 @@ int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
                             void *out, int32_t total_tokens, int32_t dtype, void *stream) {
     return prefill_impl(q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out, total_tokens, dtype,
                         stream, nullptr);
+}
+
+int kev_packed_attn_prefill_noalloc(const void *q, const void *k, const void *v,
+                                    const int32_t *cu_seqlens, int32_t n_seg,
+                                    int32_t heads, int32_t kv_heads, int32_t head_dim,
+                                    void *out, int32_t total_tokens, int32_t dtype, void *stream_) {
+    int rc = check_prefill_args(q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out, total_tokens, dtype,
+                                nullptr);
+    if (rc || n_seg == 0) return rc;
+    PrefillPlan pl;
+    rc = plan_prefill(n_seg, total_tokens, heads, kv_heads, dtype, &pl);
+    if (rc) return rc;
+    if ((size_t)pl.lay.total * sizeof(int32_t) > kScratchBytes - kScratchTables) return KEV_ERR_SCRATCH_LIMIT;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
+    int32_t *sp = nullptr;
+    rc = scratch_on(dev, &sp);
+    if (rc) return rc;
+    return enqueue_prefill(q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out, total_tokens, dtype, nullptr,
+                           pl, sp + kScratchTables / sizeof(int32_t), sp, static_cast<hipStream_t>(stream_),
+                           /*may_log=*/false);
 }
 
 int kev_packed_attn_prefill_slots(const void *q, const void *k, const void *v,
@@ -591,13 +638,25 @@ int kev_get_device_errors(void *stream_, int32_t *flags_out) {
     int32_t *err = nullptr;
     int rc = error_word(dev, stream, &err);
     if (rc) return rc;
-    int32_t v = 0;
+    int32_t v = 0, w = 0;
     // Stream order: the read follows every kernel enqueued on this stream before the call, and
     // the clear follows the read.
     if (hipMemcpyAsync(&v, err, sizeof v, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-        hipMemsetAsync(err, 0, sizeof v, stream) != hipSuccess || hipStreamSynchronize(stream) != hipSuccess)
+        hipMemsetAsync(err, 0, sizeof v, stream) != hipSuccess)
         return KEV_ERR_DEVICE;
-    *flags_out = v;
+    // The no-allocation prefill's error word (one per device, shared by every stream).
+    int32_t *sp = nullptr;
+    {
+        State &st = state();
+        std::lock_guard<std::mutex> lock(st.mu);
+        auto it = st.scratch_ptr.find(dev);
+        if (it != st.scratch_ptr.end()) sp = it->second;
+    }
+    if (sp && (hipMemcpyAsync(&w, sp, sizeof w, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+               hipMemsetAsync(sp, 0, sizeof w, stream) != hipSuccess))
+        return KEV_ERR_DEVICE;
+    if (hipStreamSynchronize(stream) != hipSuccess) return KEV_ERR_DEVICE;
+    *flags_out = v | w;
     return KEV_OK;
 }
 

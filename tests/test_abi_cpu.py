@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert K.status_string(code) not in ("", "unknown status")
     assert K.status_string(42) == "unknown status"
 
