@@ -77,7 +77,7 @@ struct Req {
     int r, slot, L;
 };
 template <bool PAGED>
-__device__ inline Req ranked_request(int b_req, const DecodeArgs &p) {
+__device__ inline Req ranked_request(int b_req, const DecodeArgs &p, __attribute__((address_space(3))) int *keys) {
     const int lane = threadIdx.x & 63;
     int t = -1, sl = 0, ln = 0;
     if (lane < p.n_req) {
@@ -85,10 +85,24 @@ __device__ inline Req ranked_request(int b_req, const DecodeArgs &p) {
         ln = p.cache_lens[lane];
         t = req_valid<PAGED>(sl, ln, p) ? (ln + DKT - 1) / DKT : 0;
     }
+    // Every lane's tile count goes to 64 words of this wavefront's own LDS, and each lane counts
+    // the requests ranked ahead of it from broadcast reads of four counts at a time (lanes past
+    // n_req hold -1 and rank last).  A loop of 64 lane reads into scalar registers, each
+    // feeding a vector compare, took about twice as long on this path, which every workgroup
+    // runs before its first load.
+    keys[lane] = t;
+    __builtin_amdgcn_wave_barrier();
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const __attribute__((address_space(3))) i32x4 *k4 = reinterpret_cast<const __attribute__((address_space(3))) i32x4 *>(keys);
     int rank = 0;
-    for (int j = 0; j < p.n_req; ++j) {
-        const int tj = __builtin_amdgcn_readlane(t, j);
-        rank += (tj > t || (tj == t && j < lane)) ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const i32x4 v = k4[q];
+        const int j = 4 * q;
+        rank += (v.x > t || (v.x == t && j < lane)) ? 1 : 0;
+        rank += (v.y > t || (v.y == t && j + 1 < lane)) ? 1 : 0;
+        rank += (v.z > t || (v.z == t && j + 2 < lane)) ? 1 : 0;
+        rank += (v.w > t || (v.w == t && j + 3 < lane)) ? 1 : 0;
     }
     const uint64_t hit = __ballot(lane < p.n_req && rank == b_req);
     const int f = hit ? (int)__builtin_ctzll(hit) : 0;   // ranks are a permutation: always hit
@@ -147,7 +161,10 @@ void decode_bf16_kernel(DecodeArgs p) {
     const int g = ublk % KVH;
     int r, slot, L;
     if (!SPLIT && p.ranked) {
-        const Req q = ranked_request<PAGED>(ublk / KVH, p);
+        // ranking scratch: the first 256 bytes of this wavefront's own tile buffer, which it
+        // fills only after the ranking
+        const Req q = ranked_request<PAGED>(
+            ublk / KVH, p, reinterpret_cast<__attribute__((address_space(3))) int *>((lds_t *)smem + wave * 2 * TB));
         r = q.r;
         slot = q.slot;
         L = q.L;
