@@ -226,21 +226,48 @@ bool fetch(std::vector<int32_t> &dst, const int32_t *src, size_t n, hipStream_t 
                       hipStreamSynchronize(stream) == hipSuccess);
 }
 
+// XCDs of a device (workgroups of a launch are dealt to them round-robin), 1 if unknown.
+int xcd_count(int dev) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        return 1;
+    }
+    return n;
+}
+
+// Item streams of a bf16 prefill (1 = one question-major work list).  When an XCD would
+// otherwise share a (question, KV head) pair with another XCD (fewer KV heads than XCDs), the
+// questions are split into n_xcd / kv_heads streams and every XCD serves one (stream, KV head)
+// pair, so a question's K/V rows are fetched into one L2 only.  Used for two streams with at
+// least 4 questions each way, at most 64 questions (the one-wavefront work-list pass deals
+// them); KEV_XCD_STREAMS=0 turns it off.
+int32_t prefill_streams(int32_t kv_heads, int32_t n_seg, int n_xcd, int32_t dtype) {
+    if (dtype != KEV_BF16 || n_xcd <= kv_heads || n_xcd % kv_heads != 0) return 1;
+    if (const char *e = std::getenv("KEV_XCD_STREAMS"))
+        if (e[0] == '0') return 1;
+    const int32_t n = n_xcd / kv_heads;
+    if (n > 2 || n > kStreamsMax || n_seg > 64 || n_seg < 4 * n) return 1;
+    return n;
+}
+
 // Schedule-table geometry of a prefill call.
 struct PrefillPlan {
-    int32_t block_rows, hist_len;
-    int64_t n_max;
+    int32_t block_rows, hist_len, n_streams, n_xcd;
+    int64_t n_max;   // item capacity per stream
     ScheduleLayout lay;
 };
 
-int plan_prefill(int32_t n_seg, int32_t total_tokens, int32_t heads, int32_t kv_heads, int32_t dtype,
+int plan_prefill(int32_t n_seg, int32_t total_tokens, int32_t heads, int32_t kv_heads, int32_t dtype, int dev,
                  PrefillPlan *pl) {
     pl->block_rows = block_rows_for(heads, kv_heads, dtype);
     pl->n_max = max_items(total_tokens, n_seg, pl->block_rows);
+    pl->n_xcd = xcd_count(dev);
+    pl->n_streams = prefill_streams(kv_heads, n_seg, pl->n_xcd, dtype);
     const int64_t hist_len = qblocks(total_tokens, pl->block_rows) + 2;
-    if (hist_len > INT32_MAX || pl->n_max > INT32_MAX / 2) return KEV_ERR_INVALID_ARG;
+    if (hist_len > INT32_MAX || pl->n_max * pl->n_streams > INT32_MAX / 4) return KEV_ERR_INVALID_ARG;
     pl->hist_len = (int32_t)hist_len;
-    pl->lay = schedule_layout(n_seg, pl->hist_len, pl->n_max);
+    pl->lay = schedule_layout(n_seg, pl->hist_len, pl->n_max * pl->n_streams);
     return KEV_OK;
 }
 
@@ -274,16 +301,16 @@ int enqueue_prefill(const void *q, const void *k, const void *v, const int32_t *
                     hipStream_t stream, bool may_log = true) {
     ScheduleArgs sa{cu_seqlens, n_seg, total_tokens, pl.block_rows, pl.hist_len,
                     prefill_order(total_tokens, head_dim, dtype), pl.n_max, ws, err,
-                    pre ? pre->prefix_lens : nullptr};
+                    pre ? pre->prefix_lens : nullptr, pl.n_streams};
     int rc = to_status(launch_schedule(sa, stream));
     if (rc) return rc;
     if (may_log && log_enabled()) {
         std::vector<int32_t> n;
         if (!fetch(n, ws, 1, stream)) return KEV_ERR_DEVICE;
         std::fprintf(stderr, "[kev] prefill: %d questions, %d tokens, %d/%d heads, d=%d; %d items of %d rows "
-                             "(capacity %lld), workspace %lld B%s\n",
+                             "(capacity %lld), %d stream(s) over %d XCDs, workspace %lld B%s\n",
                      n_seg, total_tokens, heads, kv_heads, head_dim, n[0], pl.block_rows, (long long)pl.n_max,
-                     (long long)(pl.lay.total * 4), pre ? ", slot prefixes" : "");
+                     pl.n_streams, pl.n_xcd, (long long)(pl.lay.total * 4), pre ? ", slot prefixes" : "");
     }
     if (total_tokens == 0) return KEV_OK;   // only empty questions; cu_seqlens still checked
 
@@ -306,7 +333,10 @@ int enqueue_prefill(const void *q, const void *k, const void *v, const int32_t *
         pa.row_blocks = sh.row_blocks;
         pa.block_rows = sh.block_rows;
         pa.wg_per_kvh = sh.wg_per_kvh;
-        const int64_t grid = pl.n_max * kv_heads * sh.wg_per_kvh;
+        pa.n_streams = pl.n_streams;
+        pa.n_xcd = pl.n_xcd;
+        pa.stream_cap = (int32_t)pl.n_max;
+        const int64_t grid = pl.n_max * pl.n_streams * kv_heads * sh.wg_per_kvh;
         if (grid > INT32_MAX) return KEV_ERR_INVALID_ARG;
         if (pre) {
             pa.slot_ids = pre->slot_ids;
@@ -346,11 +376,11 @@ int prefill_impl(const void *q, const void *k, const void *v, const int32_t *cu_
         rc = check_seqlens_on_host(cu_seqlens, n_seg, total_tokens, stream);
         if (rc) return rc;
     }
-    PrefillPlan pl;
-    rc = plan_prefill(n_seg, total_tokens, heads, kv_heads, dtype, &pl);
-    if (rc) return rc;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
+    PrefillPlan pl;
+    rc = plan_prefill(n_seg, total_tokens, heads, kv_heads, dtype, dev, &pl);
+    if (rc) return rc;
     int32_t *err = nullptr;
     rc = error_word(dev, stream, &err);
     if (rc) return rc;
@@ -510,12 +540,12 @@ int kev_packed_attn_prefill_noalloc(const void *q, const void *k, const void *v,
     int rc = check_prefill_args(q, k, v, cu_seqlens, n_seg, heads, kv_heads, head_dim, out, total_tokens, dtype,
                                 nullptr);
     if (rc || n_seg == 0) return rc;
-    PrefillPlan pl;
-    rc = plan_prefill(n_seg, total_tokens, heads, kv_heads, dtype, &pl);
-    if (rc) return rc;
-    if ((size_t)pl.lay.total * sizeof(int32_t) > kScratchBytes - kScratchTables) return KEV_ERR_SCRATCH_LIMIT;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
+    PrefillPlan pl;
+    rc = plan_prefill(n_seg, total_tokens, heads, kv_heads, dtype, dev, &pl);
+    if (rc) return rc;
+    if ((size_t)pl.lay.total * sizeof(int32_t) > kScratchBytes - kScratchTables) return KEV_ERR_SCRATCH_LIMIT;
     int32_t *sp = nullptr;
     rc = scratch_on(dev, &sp);
     if (rc) return rc;
@@ -689,7 +719,7 @@ int kev_schedule_device(const int32_t *cu_seqlens, int32_t n_seg, int32_t total_
     rc = workspace_acquire(dev, stream, (size_t)lay.total * sizeof(int32_t), &ws);
     if (rc) return rc;
     int32_t *w = static_cast<int32_t *>(ws.ptr);
-    ScheduleArgs sa{cu_seqlens, n_seg, total_tokens, block_rows, (int32_t)hist_len, order, n_max, w, err, nullptr};
+    ScheduleArgs sa{cu_seqlens, n_seg, total_tokens, block_rows, (int32_t)hist_len, order, n_max, w, err, nullptr, 1};
     rc = to_status(launch_schedule(sa, stream));
     std::vector<int32_t> n, items;
     if (!rc && !fetch(n, w, 1, stream)) rc = KEV_ERR_DEVICE;

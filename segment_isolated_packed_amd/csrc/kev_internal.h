@@ -19,12 +19,17 @@ struct ScheduleArgs {
     int32_t block_rows;
     int32_t hist_len;         // >= max query blocks per question + 2
     int32_t order;            // kOrderQuestion or kOrderLevel
-    int64_t n_max_items;      // item capacity the workspace was laid out for
+    int64_t n_max_items;      // item capacity (per stream) the workspace was laid out for
     int32_t *ws;              // workspace, see schedule_layout()
     int32_t *err;             // device error word
     // chunked prefill: rows already cached per question; with at most 64 questions the
     // question order then follows the blocks of prefix + chunk (the work of the last block)
     const int32_t *prefix_lens;
+    // n_streams > 1 (at most 64 questions, question-major order): questions are dealt to
+    // n_streams streams, longest first, each to the stream with the least work so far; stream s
+    // lists its questions' items question-major at records [s * n_max_items, ...), and the
+    // records after its last item carry length -1
+    int32_t n_streams;
 };
 
 
@@ -38,6 +43,10 @@ struct PrefillArgs {
     int32_t heads, kv_heads, group;     // group = heads / kv_heads
     int32_t heads_per_wg, row_blocks, block_rows, n_hgroups;   // fp32 path
     int32_t wg_per_kvh;                 // bf16 path: workgroups per item and KV head
+    // bf16 path, n_streams > 1: workgroup b runs on XCD x = b % n_xcd (workgroups are dealt to
+    // the XCDs round-robin) and serves KV head x % kv_heads of stream x / kv_heads, as that
+    // pair's (b / n_xcd)-th workgroup; stream s's records start at s * stream_cap
+    int32_t n_streams, n_xcd, stream_cap;
     float scale_log2;                   // log2(e) / sqrt(head_dim)
     // Chunked prefill only: question s continues the prefix_lens[s] rows cached in slot
     // slot_ids[s] of the pool [n_slots][2][kv_heads][capacity][head_dim].

@@ -288,14 +288,27 @@ void prefill_bf16_kernel(PrefillArgs p) {
 
     // The item record and the item count are read together (one round trip); records past
     // the count exist (the record array covers the whole grid) and are not used.
-    const int per_item = p.kv_heads * p.wg_per_kvh;
-    const int item = blockIdx.x / per_item;
+    int item, kvh, w;
+    if (p.n_streams > 1) {
+        // XCD-aware: this workgroup runs on XCD x and serves one (stream, KV head) pair there,
+        // so the XCD's L2 holds that pair's K/V rows only (see PrefillArgs)
+        const int x = blockIdx.x % p.n_xcd, kk = blockIdx.x / p.n_xcd;
+        kvh = x % p.kv_heads;
+        const int idx = kk / p.wg_per_kvh;
+        w = kk - idx * p.wg_per_kvh;
+        item = (x / p.kv_heads) * p.stream_cap + idx;
+    } else {
+        const int per_item = p.kv_heads * p.wg_per_kvh;
+        item = blockIdx.x / per_item;
+        const int rem = blockIdx.x - item * per_item;
+        kvh = rem % p.kv_heads;   // KV head fastest: see above
+        w = rem / p.kv_heads;
+    }
     const __attribute__((address_space(4))) int *recs = (const __attribute__((address_space(4))) int *)p.rec;
     const int a = recs[4 * item], L = recs[4 * item + 1], t = recs[4 * item + 2], sq = recs[4 * item + 3];
     const int32_t n_items = ((const __attribute__((address_space(4))) int *)p.sched)[0];
-    if (item >= n_items) return;
-    const int rem = blockIdx.x - item * per_item;
-    const int kvh = rem % p.kv_heads, w = rem / p.kv_heads;   // KV head fastest: see above
+    if (p.n_streams > 1 ? (n_items == 0 || L < 0) : item >= n_items) return;   // past the work list
+    const int rem = w * p.kv_heads + kvh;   // the workgroup's place in its item (0: reports errors)
     const int G = p.group;
 
     const int item_row0 = t * p.block_rows;

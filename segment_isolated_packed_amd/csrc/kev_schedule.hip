@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
     __shared__ int32_t t_cu[kLds + 1], t_hist[kLds], t_fill[kLds], t_cnt[kLds], t_start[kLds],
         t_sigma[kLds], t_qoff[kLds];
     const int tid = threadIdx.x;
-    const ScheduleLayout lay = schedule_layout(a.n_seg, a.hist_len, a.n_max_items);
+    const ScheduleLayout lay = schedule_layout(a.n_seg, a.hist_len, a.n_max_items);   // one stream
     int32_t *ws = a.ws;
     int32_t *items = ws + lay.items;
     int4 *rec = reinterpret_cast<int4 *>(ws + lay.rec);
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(ScheduleArgs a) {
 // in a lane: no LDS tables and no workgroup barriers, so the pass costs little more than one
 // read of cu_seqlens and the stores of the list.  Ties in block count go by question index.
 __global__ __launch_bounds__(64) void schedule_small_kernel(ScheduleArgs a) {
-    const ScheduleLayout lay = schedule_layout(a.n_seg, a.hist_len, a.n_max_items);
+    const ScheduleLayout lay = schedule_layout(a.n_seg, a.hist_len, a.n_max_items * max(a.n_streams, 1));
     int32_t *ws = a.ws;
     int32_t *items = ws + lay.items;
     int4 *rec = reinterpret_cast<int4 *>(ws + lay.rec);
@@ -254,6 +254,60 @@ __global__ __launch_bounds__(64) void schedule_small_kernel(ScheduleArgs a) {
             for (int j = 0; j < a.n_seg; ++j) c += __builtin_amdgcn_readlane(nb, j) > t ? 1 : 0;
             above += c;
         }
+    } else if (a.n_streams > 1) {
+        // Streams of whole questions: in rank order, each question joins the stream with the
+        // least work so far (work of a question: the key blocks its items read, prefix included),
+        // and takes the next items of that stream.  Stream s owns records [s * cap, (s+1) * cap);
+        // the records after its last item get length -1.
+        const int pre = (a.prefix_lens && lane < a.n_seg && nb > 0) ? max(a.prefix_lens[lane], 0) : 0;
+        const float work = (float)nb * (float)qblocks(pre, a.block_rows) + 0.5f * (float)nb * (float)(nb + 1);
+        const int64_t cap = a.n_max_items;
+        float load[kStreamsMax];
+        int fill[kStreamsMax];
+#pragma unroll
+        for (int st = 0; st < kStreamsMax; ++st) {
+            load[st] = 0.f;
+            fill[st] = 0;
+        }
+        int my_stream = 0, my_pos = 0;
+        for (int k = 0; k < a.n_seg; ++k) {
+            const uint64_t who = __ballot(lane < a.n_seg && rank == k);
+            const int ql = (int)__builtin_ctzll(who);   // ranks are a permutation: always hit
+            const int qnb = __builtin_amdgcn_readlane(nb, ql);
+            if (qnb == 0) continue;
+            const float qw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(work), ql));
+            int best = 0;
+            float bl = load[0];
+#pragma unroll
+            for (int st = 1; st < kStreamsMax; ++st)
+                if (st < a.n_streams && load[st] < bl) {
+                    best = st;
+                    bl = load[st];
+                }
+            int at = 0;
+#pragma unroll
+            for (int st = 0; st < kStreamsMax; ++st)
+                if (st == best) {
+                    at = fill[st];
+                    fill[st] += qnb;
+                    load[st] += qw;
+                }
+            if (lane == ql) {
+                my_stream = best;
+                my_pos = at;
+            }
+        }
+        for (int k = 0; k < nb; ++k) {
+            const int64_t p = my_stream * cap + my_pos + k;
+            const int t = nb - 1 - k;
+            items[2 * p] = lane;
+            items[2 * p + 1] = t;
+            rec[p] = make_int4(q0, len, t, lane);
+        }
+#pragma unroll
+        for (int st = 0; st < kStreamsMax; ++st)
+            if (st < a.n_streams)
+                for (int64_t p = fill[st] + lane; p < cap; p += 64) rec[st * cap + p] = make_int4(0, -1, 0, 0);
     } else {
         for (int k = 0; k < nb; ++k) {
             const int p = before + k, t = nb - 1 - k;

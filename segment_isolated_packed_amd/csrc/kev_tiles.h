@@ -54,7 +54,10 @@ constexpr int32_t kF32BlockRows = 64;   // fp32 path: one wavefront of 64 rows p
 constexpr int32_t kOrderQuestion = 0;
 constexpr int32_t kOrderLevel = 1;
 
-// Workspace layout of the scheduler (int32 units):
+// Most item streams of an XCD-aware prefill launch (the work-list pass keeps one count per stream).
+constexpr int32_t kStreamsMax = 8;
+
+// Workspace layout of the scheduler (int32 units; max_items counts every stream's records):
 //   [0] n_items  [1..3] unused  [4..] hist[hist_len] | fill[hist_len] | cnt[hist_len] |
 //   start[hist_len] | sigma[n_seg] | qoff[n_seg] | items[2 * max_items] (question, t) |
 //   rec[4 * max_items] ({question start, question length, t, question index}, 16-byte aligned)
