@@ -24,7 +24,7 @@
 // head; with the scheduler's question-major order, the workgroups resident on
 // one XCD then read the K/V rows of one (question, KV head) from its L2.
 //
-// Occupancy.  A workgroup uses 64 KB of LDS and at most 256 registers per lane,
+// Occupancy.  A workgroup uses 80 KB of LDS and at most 256 registers per lane,
 // so two workgroups share each CU and every SIMD runs two wavefronts that belong
 // to different workgroups.  Their barriers are independent, so one wavefront's
 // MFMA work can overlap the other's softmax work.
@@ -43,11 +43,12 @@
 // (tile_pv below), so the common tile spends one FMA and one exp per score, a
 // bf16 conversion per pair and a dot product per pair for the row sum.
 //
-// Pipeline.  Tiles are 32 keys.  K and V each have four LDS stages and direct
-// loads run three tiles ahead.  Iteration j starts with the scores of tile j
+// Pipeline.  Tiles are 32 keys.  K and V each have five LDS stages (80 KB per
+// workgroup, two workgroups per CU fill its 160 KB) and direct loads run four
+// tiles ahead.  Iteration j starts with the scores of tile j
 // already issued on MFMA.  The wavefront waits for its own loads of K(j+1) and
 // V(j), meets the others at one barrier (which also retires all reads of K(j)
-// and V(j-1), so their stages take K(j+4) and V(j+3)), reads every fragment of
+// and V(j-1), so their stages take K(j+5) and V(j+4)), reads every fragment of
 // V(j) and then K(j+1) into registers at once, takes the softmax of tile j while
 // those reads land, runs P.V of tile j and issues the scores of tile j+1, which
 // execute while it waits at the next barrier.  The loop is unrolled by the
@@ -80,7 +81,7 @@ using namespace core;
 
 constexpr int KT = 32;      // keys per tile
 constexpr int NWAVE = 4;    // wavefronts per workgroup
-constexpr int NS = 4;       // LDS stages per tensor (loads run NS-1 tiles ahead)
+constexpr int NS = 5;       // LDS stages per tensor (loads run NS-1 tiles ahead)
 
 template <int D>
 struct Cfg {
@@ -92,6 +93,8 @@ struct Cfg {
     static constexpr int TB = KT * D * 2;                // bytes per tile
     static constexpr int LDS = 2 * NS * TB;
     static_assert(IPT % NWAVE == 0 && NIT >= 1, "loads must split evenly");
+    static_assert(NS >= 4 && NS <= 5, "the loop is unrolled for four or five stages; the epilogue takes"
+                                      " three K stages and one V stage that no wavefront still reads");
 };
 
 // Direct loads of K or V tiles by NW wavefronts.  Wavefront w fills tile rows
@@ -450,6 +453,10 @@ void prefill_bf16_kernel(PrefillArgs p) {
             if (j0 + 3 >= n_tiles) break;
             iteration(j0 + 3, std::integral_constant<int, 3 % NS>{});
         }
+        if (NS > 4) {
+            if (j0 + 4 >= n_tiles) break;
+            iteration(j0 + 4, std::integral_constant<int, 4 % NS>{});
+        }
     }
 
     wait_vmcnt<0>();   // no direct load may outlive the workgroup's LDS
@@ -460,7 +467,7 @@ void prefill_bf16_kernel(PrefillArgs p) {
     // the swizzled row layout) and stores whole rows from there: D/8 lanes per row, 16 B
     // each.  Free stages: after the last barrier the other wavefronts read only K stage
     // n_tiles % NS and V stage (n_tiles - 1) % NS, and no direct load is in flight, so
-    // wavefronts 0..2 take the other three K stages and wavefront 3 takes V stage
+    // wavefronts 0..2 take the next three K stages after it and wavefront 3 takes V stage
     // n_tiles % NS.  LDS operations of one wavefront complete in order, so the reads see
     // the writes without a barrier.
     const float l_tot = sum_halves(st.l);
