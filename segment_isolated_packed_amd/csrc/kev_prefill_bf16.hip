@@ -53,6 +53,13 @@
 // those reads land, runs P.V of tile j and issues the scores of tile j+1, which
 // execute while it waits at the next barrier.  The loop is unrolled by the
 // stage count, so all LDS addresses carry the stage as an immediate offset.
+// While it issues those 16 MFMAs the wavefront holds a raised issue priority,
+// so that when both wavefronts of a SIMD have work ready the one feeding the
+// matrix unit goes first and the other's softmax fills the gaps.  The softmax
+// scale is waited for before the loop: a scalar load still in flight there
+// would turn the first use of the scale in every tile into a wait for all
+// outstanding LDS reads (scalar loads return out of order), and the softmax
+// would then wait for the fragment reads it does not use.
 // Only tiles inside the item's own question and at or left of its diagonal are
 // loaded; the causal select (-inf, not a multiply) is applied only to tiles
 // that cross a wavefront's diagonal or the end of the question.
@@ -265,6 +272,7 @@ __device__ __forceinline__ void tile_pv(const f32x16 &s, const bf16x8 *vf, float
         lt = tile_p(s, c, -st.m, pb);
     }
     st.l += lt;
+    __builtin_amdgcn_s_setprio(3);   // dropped again once the scores of the next tile are issued
     tile_o<D>(pb, vf, st);
 }
 
@@ -361,7 +369,8 @@ void prefill_bf16_kernel(PrefillArgs p) {
         for (int i = 0; i < 16; ++i) st.o[db][i] = 0.f;
     st.m = -INFINITY;
     st.l = 0.f;
-    const float c = p.scale_log2;
+    float c = p.scale_log2;   // in a register before the loop (see Pipeline)
+    asm volatile("" : "+s"(c));
 
     TileLoader<D, NWAVE, PREFIX> ld;
     ld.init(kg, vg, kv_stride, wg_key_end, wave, pk, pv, P);
@@ -439,6 +448,7 @@ void prefill_bf16_kernel(PrefillArgs p) {
             if (j >= n_full) mask_tile<D>(s, j * KT, P + qrow, P + L);
             tile_pv<D>(s, vf, c, st);
             if (j + 1 < my_tiles) s = score();
+            __builtin_amdgcn_s_setprio(0);
         }
     };
     for (int j0 = 0; j0 < n_tiles; j0 += NS) {
