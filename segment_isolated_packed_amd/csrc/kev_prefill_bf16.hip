@@ -73,7 +73,9 @@
 // chunk rows]: key tiles wholly inside the prefix are loaded from the slot
 // (contiguous rows), tiles wholly inside the chunk from the packed K/V, and the
 // one tile that straddles the boundary per lane from either.  The diagonal and
-// the question end move right by P; everything else is unchanged.
+// the question end move right by P.  A question's K/V here can fill an XCD's L2,
+// so the chunk's query rows and outputs go through with the non-temporal hint
+// (read and written once, they should not displace K/V lines).
 #include <type_traits>
 
 #include "../../include/kev.h"
@@ -387,7 +389,12 @@ void prefill_bf16_kernel(PrefillArgs p) {
                              ((int64_t)(a + min(qrow, L - 1)) * p.heads + head) * D + half * 8;
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc)
-            asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[dc]) : "v"(qp + dc * 16) : "memory");
+        {
+            if (PREFIX)   // non-temporal: the rows are read once and should not displace K/V in L2
+                asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(qf[dc]) : "v"(qp + dc * 16) : "memory");
+            else
+                asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[dc]) : "v"(qp + dc * 16) : "memory");
+        }
     }
 
     // Issue order: K(0); then, per (virtual) iteration i, K(i+NS) and V(i+NS-1).  At the
@@ -503,7 +510,10 @@ void prefill_bf16_kernel(PrefillArgs p) {
     for (int k = 0; k < 32 / GM::RPI; ++k) {
         const int r = k * GM::RPI + rr;
         const u32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(ob + GM::off(r, cc));
-        if (row0 + r < L) *reinterpret_cast<u32x4 *>(orow + r * rstride) = x;
+        if (row0 + r < L) {
+            if (PREFIX) __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(orow + r * rstride));
+            else *reinterpret_cast<u32x4 *>(orow + r * rstride) = x;
+        }
     }
 }
 

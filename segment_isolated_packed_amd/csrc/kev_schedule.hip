@@ -297,9 +297,13 @@ __global__ __launch_bounds__(64) void schedule_small_kernel(ScheduleArgs a) {
                 my_pos = at;
             }
         }
+        // A chunk that continues a cached prefix lists its query blocks in ascending order:
+        // a prefix's K/V (up to an L2's worth) is then swept by the blocks of the chunk in the
+        // order they start, so later blocks find more of it still resident.  Fresh questions
+        // rank last in their stream and keep the descending order (longest item first).
         for (int k = 0; k < nb; ++k) {
             const int64_t p = my_stream * cap + my_pos + k;
-            const int t = nb - 1 - k;
+            const int t = pre > 0 ? k : nb - 1 - k;
             items[2 * p] = lane;
             items[2 * p + 1] = t;
             rec[p] = make_int4(q0, len, t, lane);
