@@ -22,7 +22,10 @@
 // each XCD has its own L2.  The KV head is the fastest-varying part of the
 // workgroup index, so when kv_heads divides 8 every XCD serves a single KV
 // head; with the scheduler's question-major order, the workgroups resident on
-// one XCD then read the K/V rows of one (question, KV head) from its L2.
+// one XCD then read the K/V rows of one (question, KV head) from its L2.  With
+// fewer KV heads than XCDs (kv_heads = 4) the scheduler deals the questions to
+// two item streams instead and each XCD serves one (stream, KV head) pair
+// (PrefillArgs::n_streams), so no two XCDs fetch the same question's K/V.
 //
 // Occupancy.  A workgroup uses 80 KB of LDS and at most 256 registers per lane,
 // so two workgroups share each CU and every SIMD runs two wavefronts that belong
