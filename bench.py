@@ -446,7 +446,7 @@ def main():
             other_res[name] = {"tokens": oc.total_tokens, "effective_gflop": oc.effective_flops() / 1e9,
                                "call_ms": cms, "call_tflops": oc.effective_flops() / (cms * 1e-3) / 1e12,
                                "kernel_ms": kms, "kernel_tflops": ktf, "kernel_frac": ktf / PEAK_BF16_TFLOPS,
-                               "kernel_hbm_bytes_per_launch": traffic_for("prefill_bf16_kernel", name,
+                               "kernel_hbm_bytes_per_launch": traffic_for("prefill_r48_kernel", name,
                                                                           source_hash(PREFILL_SOURCES)),
                                "workload": W.PREFILL_DESCRIPTIONS[name]}
             del oq, ok_, ov, oout
@@ -480,9 +480,9 @@ def main():
             "kernel_ms": ck_ms, "kernel_tflops": cc.effective_flops() / (ck_ms * 1e-3) / 1e12,
             "effective_gflop": cc.effective_flops() / 1e9, "algorithmic_mb": cc.algorithmic_bytes() / 1e6,
             "workload": W.CHUNKED_DESCRIPTION, "seed": cc.seed,
-            "kernel_hbm_bytes_per_launch": traffic_for("prefill_bf16_kernel_prefix", "chunked_qwen25_7b",
+            "kernel_hbm_bytes_per_launch": traffic_for("prefill_r48_kernel_prefix", "chunked_qwen25_7b",
                                                        source_hash(PREFILL_SOURCES)),
-            "call": "kev_chunked_prefill_slots: scheduler + prefill_bf16_kernel<128, prefix> + K/V append"}
+            "call": "kev_chunked_prefill_slots: scheduler + prefill_r48_kernel<true> (prefix) + K/V append"}
         del cq, ck, cv, cpool, cout
 
     pre_ms = [e[0].elapsed_time(e[1]) for e in events] if do_pre else [float("nan")]
@@ -525,8 +525,8 @@ def main():
         "roofline": {
             "bound": "mfma", "achieved": kernel_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": kernel_tflops / PEAK_BF16_TFLOPS if kernel_tflops else None,
-            "traffic": traffic_for("prefill_bf16_kernel", args.workload, source_hash(PREFILL_SOURCES)),
-            "kernel": "kev prefill_bf16_kernel<128, false> (the attention kernel; events recorded "
+            "traffic": traffic_for("prefill_r48_kernel", args.workload, source_hash(PREFILL_SOURCES)),
+            "kernel": "kev prefill_r48_kernel<false> (the head_dim-128 attention kernel; events recorded "
                       "by the library around its launch on the call's stream)",
             "kernel_ms": pre_kernel_ms,
             "algorithmic_flops_per_launch": flops,

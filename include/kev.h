@@ -125,12 +125,12 @@ int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
  *
  * Its work list and its error word live in a device array of 4 MiB that the
  * library holds on every GPU it runs on until the process ends.  A call whose
- * work list needs more (about 3.5 M tokens at the 32-row blocks of the 32/8-head
- * shape, fewer with more questions) returns KEV_ERR_SCRATCH_LIMIT and enqueues
- * nothing.  Every call on one GPU shares that array, and a call overwrites what
- * the previous one left there: calls that overlap on one GPU (on different
- * streams, or from different host threads without ordering) race and are not
- * allowed.  Device-array errors set bits in the array's own error word, which
+ * work list needs more (about 5 M tokens at the 48-row blocks of the 32/8-head,
+ * head_dim-128 shape, fewer with more questions) returns KEV_ERR_SCRATCH_LIMIT
+ * and enqueues nothing.  Every call on one GPU shares that array, and a call
+ * overwrites what the previous one left there: calls that overlap on one GPU
+ * (on different streams, or from different host threads without ordering) race
+ * and are not allowed.  Device-array errors set bits in the array's own error word, which
  * the next kev_get_device_errors on that GPU (any stream) reports and clears.
  * KEV_CHECK and KEV_LOG are ignored (both would copy to the host and wait).
  */

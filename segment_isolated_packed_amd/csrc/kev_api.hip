@@ -202,9 +202,9 @@ bool prefill_supported(int32_t head_dim, int32_t dtype) {
     return false;
 }
 
-int32_t block_rows_for(int32_t heads, int32_t kv_heads, int32_t dtype) {
+int32_t block_rows_for(int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype) {
     if (dtype == KEV_F32) return kF32BlockRows;
-    return prefill_shape_bf16(heads, kv_heads).block_rows;
+    return prefill_shape_bf16(heads, kv_heads, head_dim).block_rows;
 }
 
 // Item order of a prefill call: question-major, so concurrently running workgroups share one
@@ -258,9 +258,9 @@ struct PrefillPlan {
     ScheduleLayout lay;
 };
 
-int plan_prefill(int32_t n_seg, int32_t total_tokens, int32_t heads, int32_t kv_heads, int32_t dtype, int dev,
-                 PrefillPlan *pl) {
-    pl->block_rows = block_rows_for(heads, kv_heads, dtype);
+int plan_prefill(int32_t n_seg, int32_t total_tokens, int32_t heads, int32_t kv_heads, int32_t head_dim,
+                 int32_t dtype, int dev, PrefillPlan *pl) {
+    pl->block_rows = block_rows_for(heads, kv_heads, head_dim, dtype);
     pl->n_max = max_items(total_tokens, n_seg, pl->block_rows);
     pl->n_xcd = xcd_count(dev);
     pl->n_streams = prefill_streams(kv_heads, n_seg, pl->n_xcd, dtype);
@@ -329,7 +329,7 @@ int enqueue_prefill(const void *q, const void *k, const void *v, const int32_t *
     pa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
     pa.err = err;
     if (dtype == KEV_BF16) {
-        const PrefillShape sh = prefill_shape_bf16(heads, kv_heads);
+        const PrefillShape sh = prefill_shape_bf16(heads, kv_heads, head_dim);
         pa.row_blocks = sh.row_blocks;
         pa.block_rows = sh.block_rows;
         pa.wg_per_kvh = sh.wg_per_kvh;
@@ -379,7 +379,7 @@ int prefill_impl(const void *q, const void *k, const void *v, const int32_t *cu_
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
     PrefillPlan pl;
-    rc = plan_prefill(n_seg, total_tokens, heads, kv_heads, dtype, dev, &pl);
+    rc = plan_prefill(n_seg, total_tokens, heads, kv_heads, head_dim, dtype, dev, &pl);
     if (rc) return rc;
     int32_t *err = nullptr;
     rc = error_word(dev, stream, &err);
@@ -522,7 +522,7 @@ const char *kev_status_string(int status) {
 int kev_prefill_block_rows(int32_t heads, int32_t kv_heads, int32_t head_dim, int32_t dtype) {
     if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0) return 0;
     if (!prefill_supported(head_dim, dtype)) return 0;
-    return block_rows_for(heads, kv_heads, dtype);
+    return block_rows_for(heads, kv_heads, head_dim, dtype);
 }
 
 int kev_packed_attn_prefill(const void *q, const void *k, const void *v,
@@ -543,7 +543,7 @@ int kev_packed_attn_prefill_noalloc(const void *q, const void *k, const void *v,
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KEV_ERR_DEVICE;
     PrefillPlan pl;
-    rc = plan_prefill(n_seg, total_tokens, heads, kv_heads, dtype, dev, &pl);
+    rc = plan_prefill(n_seg, total_tokens, heads, kv_heads, head_dim, dtype, dev, &pl);
     if (rc) return rc;
     if ((size_t)pl.lay.total * sizeof(int32_t) > kScratchBytes - kScratchTables) return KEV_ERR_SCRATCH_LIMIT;
     int32_t *sp = nullptr;

@@ -10,13 +10,20 @@
 // softmax kept as a running max, running sum and rescaled accumulator that are
 // corrected whenever a later block raises the max (primer, section 2.4).
 //
-// Decomposition.  A work item from the scheduler is (question, block of 32*R
+// Decomposition.  A work item from the scheduler is (question, block of W*R
 // query rows); per KV head it holds G*R units of (query head of the group,
-// 32-row block), one wavefront each.  R is the smallest power of two with G*R
+// W-row block), one wavefront each.  R is the smallest power of two with G*R
 // a multiple of 4, so the units fill workgroups of exactly 4 wavefronts (one
 // per SIMD).  Unit u of workgroup w is u = 4w + wave, with row block u / G and
 // head u % G: a workgroup spans at most two adjacent row blocks, so its waves
 // need nearly the same keys.  All four read the same K/V tiles from LDS.
+// W = 48 for head_dim 128 (prefill_r48_kernel, three 16-row blocks on
+// v_mfma_f32_16x16x32_bf16) and W = 32 for head_dim 64 (prefill_bf16_kernel,
+// one 32-row block on v_mfma_f32_32x32x16_bf16).  Every wavefront issues the
+// same loads, LDS reads and barriers per key tile whatever its row count, so
+// more rows per wavefront spread that fixed cost over more MFMA work; 48 rows
+// is what the register file holds at head_dim 128 (O^T 96 and Q 48 registers
+// per lane).
 //
 // Placement.  Workgroups are dealt to the 8 XCDs round-robin by index, and
 // each XCD has its own L2.  The KV head is the fastest-varying part of the
@@ -32,14 +39,15 @@
 // to different workgroups.  Their barriers are independent, so one wavefront's
 // MFMA work can overlap the other's softmax work.
 //
-// MFMA orientation (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+// MFMA orientation (fp32 accumulation):
 //   S^T[key][q] = K_tile[key][:] . Q^T[:][q]     A = K from LDS, B = Q in VGPRs
 //   O^T[d][q]  += V^T[d][key]   . P^T[key][q]    A = V^T from LDS, B = P^T in VGPRs
-// With the query index on the lane (n = lane % 32), each lane owns one query
-// row: a row max needs one exchange between the two half-waves, the rescale of
-// O^T is lane-uniform, and P^T feeds the second MFMA straight from the first
-// one's accumulators (converted to bf16).  Staging and operand reads are
-// described in kev_mfma_core.h.
+// With the query index on the lane (n = lane % 32 on the 32x32 MFMA, lane % 16
+// on the 16x16 one), each lane owns one query row per row block: a row max
+// needs an exchange between the two half-waves (four lanes on the 16x16
+// MFMA), the rescale of O^T is lane-uniform, and P^T feeds the second MFMA
+// straight from the first one's accumulators (converted to bf16).  Staging and
+// operand reads are described in kev_mfma_core.h and at prefill_r48_kernel.
 //
 // Softmax.  The weights of a tile are taken against the running max as it
 // stands and the max only moves when a lane's tile sum leaves a fixed bound
@@ -54,11 +62,14 @@
 // and V(j-1), so their stages take K(j+5) and V(j+4)), reads every fragment of
 // V(j) and then K(j+1) into registers at once, takes the softmax of tile j while
 // those reads land, runs P.V of tile j and issues the scores of tile j+1, which
-// execute while it waits at the next barrier.  The loop is unrolled by the
-// stage count, so all LDS addresses carry the stage as an immediate offset.
-// While it issues those 16 MFMAs the wavefront holds a raised issue priority,
-// so that when both wavefronts of a SIMD have work ready the one feeding the
-// matrix unit goes first and the other's softmax fills the gaps.  The softmax
+// execute while it waits at the next barrier.  (The 48-row kernel has no room
+// to hold both fragment sets through the softmax: it reads V(j) after the
+// softmax and K(j+1) after P.V.)  The loop is unrolled by the stage count, so
+// all LDS addresses carry the stage as an immediate offset.  While it issues
+// those MFMAs (16 per tile at 32 rows, 48 at 48 rows) the wavefront holds a
+// raised issue priority, so that when both wavefronts of a SIMD have work
+// ready the one feeding the matrix unit goes first and the other's softmax
+// fills the gaps.  The softmax
 // scale is waited for before the loop: a scalar load still in flight there
 // would turn the first use of the scale in every tile into a wait for all
 // outstanding LDS reads (scalar loads return out of order), and the softmax
@@ -521,6 +532,336 @@ void prefill_bf16_kernel(PrefillArgs p) {
 }
 
 
+// ---- head_dim 128: 48 query rows per wavefront on v_mfma_f32_16x16x32_bf16 ----
+//
+// Lane (m = lane % 16, g = lane / 16).  The wavefront's rows form three 16-row blocks rb; the
+// lane owns query row rb*16 + m of each.  Key block kb (16 keys) of a 32-key tile.
+//   S^T block (kb, rb):  acc[i] = S^T[kb*16 + 4g + i][rb*16 + m]     A = K from LDS, B = Q^T
+//   O^T block (db, rb):  acc[i] = O^T[db*16 + 4g + i][rb*16 + m]     A = V^T from LDS, B = P^T
+// The P^T operand of row block rb takes the lane's 8 weights in the order (kb, i), so its
+// k-slot 8g + 4kb + i is key kb*16 + 4g + i; the V^T operand lists the keys in that same
+// order.  A row's 32 weights of a tile sit in the four lanes m, m+16, m+32, m+48.
+
+// K fragment (kb, s): row kb*16 + m, 16-byte chunk 4s + g (d = 32s + 8g .. +8).  Under the
+// head_dim-128 swizzle its byte offset in a stage is (m*256 + ((g ^ swz(m)) << 4)) ^ (s << 6),
+// plus kb*4096, so one lane base serves all eight fragments.
+__device__ __forceinline__ unsigned k16_lane() {
+    using G = Geom<128>;
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    return (unsigned)(m * 256 + ((g ^ G::swz(m)) << 4));
+}
+__device__ __forceinline__ bf16x8 k16_frag(const lds_t *stage, unsigned kl, int kb, int s) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
+                                          stage + kb * 4096 + (kl ^ (unsigned)(s << 6))));
+}
+
+// V^T fragment of d block db: two transposed reads (keys 4g + (n>>2) and 16 + 4g + (n>>2)
+// of 16-lane group g, four d values from chunk 2db + ((n>>1)&1), half n&1), which leave
+// V[key][db*16 + n] for the lane's eight keys in the P^T order.  Byte offset
+// (r0*256 + ((((n>>1)&1) ^ swz(r0)) << 4) + (n&1)*8) ^ (db << 5), plus 4096 for the
+// second read (rows 16 apart share the swizzle).
+__device__ __forceinline__ unsigned vt16_lane() {
+    using G = Geom<128>;
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    const int r0 = 4 * g + (n >> 2);
+    return (unsigned)(r0 * 256 + ((((n >> 1) & 1) ^ G::swz(r0)) << 4) + (n & 1) * 8);
+}
+__device__ __forceinline__ bf16x8 vt16_frag(const lds_t *stage, unsigned vl, int db) {
+    const lds_t *a = stage + (vl ^ (unsigned)(db << 5));
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)a);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a + 4096));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// max / sum over the four lanes of a row
+__device__ __forceinline__ float row_max4(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float row_sum4(float x) {
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+
+// P = exp2(S*c - m) in bf16 for row block rb and the lane's sum of those 8 weights (from the
+// bf16 values, as in tile_p).
+__device__ __forceinline__ float tile_p16(const f32x4 &s0, const f32x4 &s1, float c, float mneg, bf16x8 &pb) {
+    const unsigned one2 = 0x3F803F80u;
+    f32x8 e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        e[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c, mneg));
+        e[4 + i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c, mneg));
+    }
+    pb = __builtin_convertvector(e, bf16x8);
+    const u32x4 w = __builtin_bit_cast(u32x4, pb);
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm("v_dot2_f32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(w[i]), "v"(one2));
+    return acc;
+}
+
+template <bool PREFIX>
+__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_r48_kernel(PrefillArgs p) {
+    constexpr int D = 128, WR = 48;
+    using C = Cfg<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    const unsigned lds0 = (unsigned)(uintptr_t)(lds_t *)smem;
+    auto kst = [&](int s) { return (lds_t *)smem + s * C::TB; };
+    auto vst = [&](int s) { return (lds_t *)smem + (NS + s) * C::TB; };
+
+    int item, kvh, w;
+    if (p.n_streams > 1) {
+        const int x = blockIdx.x % p.n_xcd, kk = blockIdx.x / p.n_xcd;
+        kvh = x % p.kv_heads;
+        const int idx = kk / p.wg_per_kvh;
+        w = kk - idx * p.wg_per_kvh;
+        item = (x / p.kv_heads) * p.stream_cap + idx;
+    } else {
+        const int per_item = p.kv_heads * p.wg_per_kvh;
+        item = blockIdx.x / per_item;
+        const int rem = blockIdx.x - item * per_item;
+        kvh = rem % p.kv_heads;
+        w = rem / p.kv_heads;
+    }
+    const __attribute__((address_space(4))) int *recs = (const __attribute__((address_space(4))) int *)p.rec;
+    const int a = recs[4 * item], L = recs[4 * item + 1], t = recs[4 * item + 2], sq = recs[4 * item + 3];
+    const int32_t n_items = ((const __attribute__((address_space(4))) int *)p.sched)[0];
+    if (p.n_streams > 1 ? (n_items == 0 || L < 0) : item >= n_items) return;
+    const int rem = w * p.kv_heads + kvh;
+    const int G = p.group;
+
+    const int item_row0 = t * p.block_rows;
+    const int wg_row_lo = item_row0 + ((NWAVE * w) / G) * WR;
+    if (wg_row_lo >= L) return;
+
+    int P = 0;
+    const uint16_t *pk = nullptr, *pv = nullptr;
+    if constexpr (PREFIX) {
+        const int slot = p.slot_ids[sq];
+        P = p.prefix_lens[sq];
+        const bool bad_slot = slot < 0 || slot >= p.n_slots;
+        if (bad_slot || P < 0 || P > p.capacity - L) {
+            if (threadIdx.x == 0 && t == 0 && rem == 0)
+                atomicOr(p.err, (int32_t)(bad_slot ? KEV_DEVERR_SLOT : KEV_DEVERR_CACHE_LEN));
+            return;
+        }
+        const int64_t plane = (int64_t)p.capacity * D;
+        pk = static_cast<const uint16_t *>(p.pool) + ((int64_t)slot * 2 * p.kv_heads + kvh) * plane;
+        pv = pk + (int64_t)p.kv_heads * plane;
+    }
+    const int wg_key_end = P + min(item_row0 + ((NWAVE * w + NWAVE - 1) / G + 1) * WR, L);
+    const int n_tiles = (wg_key_end + KT - 1) / KT;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, m16 = lane & 15, g4 = lane >> 4;
+    const int u = NWAVE * w + wave;
+    const int rbu = u / G;
+    const int head = kvh * G + (u - rbu * G);
+    const int row0 = item_row0 + rbu * WR;
+    const int wave_key_end = row0 < L ? P + min(row0 + WR, L) : 0;
+    const int my_tiles = (wave_key_end + KT - 1) / KT;
+    const int n_full = (P + min(row0 + 1, L)) / KT;
+
+    const int64_t kv_stride = (int64_t)p.kv_heads * D;
+    const uint16_t *kg = static_cast<const uint16_t *>(p.k) + ((int64_t)a * p.kv_heads + kvh) * D;
+    const uint16_t *vg = static_cast<const uint16_t *>(p.v) + ((int64_t)a * p.kv_heads + kvh) * D;
+
+    f32x4 o[8][3];
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int rb = 0; rb < 3; ++rb) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float mrow[3], lrow[3];
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) {
+        mrow[rb] = -INFINITY;
+        lrow[rb] = 0.f;
+    }
+    float c = p.scale_log2;
+    asm volatile("" : "+s"(c));
+
+    TileLoader<D, NWAVE, PREFIX> ld;
+    ld.init(kg, vg, kv_stride, wg_key_end, wave, pk, pv, P);
+    auto kaddr = [&](int s) { return lds0 + (unsigned)(s * C::TB); };
+    auto vaddr = [&](int s) { return lds0 + (unsigned)((NS + s) * C::TB); };
+
+    // Q^T operands: qf[rb][s] holds q row row0 + rb*16 + m, d = 32s + 8g .. +8 (rows past the
+    // question read its last row)
+    bf16x8 qf[3][4];
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) {
+        const int qr = min(row0 + rb * 16 + m16, L - 1);
+        const uint16_t *qp = static_cast<const uint16_t *>(p.q) + ((int64_t)(a + qr) * p.heads + head) * D + g4 * 8;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (PREFIX)
+                asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(qf[rb][s]) : "v"(qp + s * 32) : "memory");
+            else
+                asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[rb][s]) : "v"(qp + s * 32) : "memory");
+        }
+    }
+    ld.issue(ld.kbase, ld.pkbase, 0, kaddr(0), wave);
+    for (int i = 1 - NS; i < 0; ++i) {
+        if (i + NS < n_tiles) ld.issue(ld.kbase, ld.pkbase, i + NS, kaddr(i + NS), wave);
+        if (i + NS - 1 < n_tiles) ld.issue(ld.vbase, ld.pvbase, i + NS - 1, vaddr(i + NS - 1), wave);
+    }
+    if (n_tiles >= NS) wait_vmcnt<2 * C::NIT * (NS - 1)>();
+    else wait_vmcnt<0>();
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) asm volatile("" : "+v"(qf[rb][0]), "+v"(qf[rb][1]), "+v"(qf[rb][2]), "+v"(qf[rb][3]));
+    barrier();
+
+    bf16x8 kf[2][4];
+    bf16x8 vf[8];
+    f32x4 sacc[2][3];
+    auto score = [&]() {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int rb = 0; rb < 3; ++rb) sacc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int rb = 0; rb < 3; ++rb)
+                    sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][s], qf[rb][s], sacc[kb][rb], 0, 0, 0);
+    };
+    if (my_tiles > 0) {
+        const unsigned kl = k16_lane();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) kf[kb][s] = k16_frag(kst(0), kl, kb, s);
+        score();
+    }
+
+    auto iteration = [&](const int j, auto U) {
+        constexpr int uu = decltype(U)::value;   // j % NS
+        if (j + NS - 1 < n_tiles) wait_vmcnt<2 * C::NIT * (NS - 2)>();
+        else wait_vmcnt<0>();
+        barrier();
+        if (j + NS < n_tiles) ld.issue(ld.kbase, ld.pkbase, j + NS, kaddr(uu), wave);
+        if (j + NS - 1 < n_tiles) ld.issue(ld.vbase, ld.pvbase, j + NS - 1, vaddr((uu + NS - 1) % NS), wave);
+        if (j < my_tiles) {
+            // lane bases and the mask's lane terms are rebuilt in every tile (one instruction
+            // each) rather than kept live across the loop
+            unsigned kl = k16_lane(), vl = vt16_lane();
+            int ldiff = P + row0 + m16 - 4 * g4, g4x4 = 4 * g4;
+            asm volatile("" : "+v"(kl), "+v"(vl), "+v"(ldiff), "+v"(g4x4));
+            if (j >= n_full) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int rb = 0; rb < 3; ++rb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            // key j*32 + kb*16 + 4g + i against position P + row0 + rb*16 + m
+                            const int kk = j * KT + kb * 16 + i;
+                            if (kk - rb * 16 > ldiff || kk + g4x4 >= P + L) sacc[kb][rb][i] = -INFINITY;
+                        }
+            }
+            bf16x8 pb[3];
+            float lt[3];
+            bool need = false;
+#pragma unroll
+            for (int rb = 0; rb < 3; ++rb) {
+                lt[rb] = tile_p16(sacc[0][rb], sacc[1][rb], c, -mrow[rb], pb[rb]);
+                need |= !(lt[rb] <= kGuardSum);
+            }
+            if (__any(need)) {
+                // move the max of every row where one of its four lanes left the bound
+#pragma unroll
+                for (int rb = 0; rb < 3; ++rb) {
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][rb][i]);
+                    mx = row_max4(mx) * c;
+                    if (row_max4(!(lt[rb] <= kGuardSum) ? 1.f : 0.f) > 0.f) {
+                        const float m_new = fmaxf(mrow[rb], mx);
+                        const float alpha = __builtin_amdgcn_exp2f(mrow[rb] - m_new);
+                        mrow[rb] = m_new;
+                        lrow[rb] *= alpha;
+#pragma unroll
+                        for (int db = 0; db < 8; ++db) o[db][rb] *= alpha;
+                        lt[rb] = tile_p16(sacc[0][rb], sacc[1][rb], c, -mrow[rb], pb[rb]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int rb = 0; rb < 3; ++rb) lrow[rb] += lt[rb];
+            const lds_t *vc = vst(uu);
+#pragma unroll
+            for (int db = 0; db < 8; ++db) vf[db] = vt16_frag(vc, vl, db);
+            __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+#pragma unroll
+                for (int rb = 0; rb < 3; ++rb)
+                    o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pb[rb], o[db][rb], 0, 0, 0);
+            if (j + 1 < my_tiles) {
+                const lds_t *kn = kst((uu + 1) % NS);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) kf[kb][s] = k16_frag(kn, kl, kb, s);
+                score();
+            }
+            __builtin_amdgcn_s_setprio(0);
+        }
+    };
+    for (int j0 = 0; j0 < n_tiles; j0 += NS) {
+        iteration(j0, std::integral_constant<int, 0>{});
+        if (j0 + 1 >= n_tiles) break;
+        iteration(j0 + 1, std::integral_constant<int, 1 % NS>{});
+        if (j0 + 2 >= n_tiles) break;
+        iteration(j0 + 2, std::integral_constant<int, 2 % NS>{});
+        if (j0 + 3 >= n_tiles) break;
+        iteration(j0 + 3, std::integral_constant<int, 3 % NS>{});
+        if (NS > 4) {
+            if (j0 + 4 >= n_tiles) break;
+            iteration(j0 + 4, std::integral_constant<int, 4 % NS>{});
+        }
+    }
+    wait_vmcnt<0>();
+
+    // Epilogue: each 16-row block goes through a free stage (the same stages as the 32-row
+    // kernel takes: no wavefront reads K stages after the last barrier, nor V stage n_tiles % NS).
+    float inv[3];
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) inv[rb] = 1.f / row_sum4(lrow[rb]);
+    if (row0 >= L) return;
+    using GM = Geom<D>;
+    lds_t *ob = wave < 3 ? kst((n_tiles + 1 + wave) % NS) : vst(n_tiles % NS);
+    const int rr = lane / GM::CPR, cc = lane % GM::CPR;
+    const int64_t rstride = (int64_t)p.heads * D;
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) {
+        if (row0 + rb * 16 >= L) break;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            // row m, d = db*16 + 4g .. +4: half g & 1 of chunk 2db + (g >> 1)
+            const int dofs = db * 16 + 4 * g4;
+            *reinterpret_cast<__attribute__((address_space(3))) bf16x4 *>(ob + GM::off(m16, dofs >> 3) + (dofs & 7) * 2) =
+                __builtin_convertvector(o[db][rb] * inv[rb], bf16x4);
+        }
+        uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)(a + row0 + rb * 16) * p.heads + head) * D + cc * 8;
+#pragma unroll
+        for (int k = 0; k < 16 / GM::RPI; ++k) {
+            const int r = k * GM::RPI + rr;
+            const u32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(ob + GM::off(r, cc));
+            if (row0 + rb * 16 + r < L) {
+                if (PREFIX) __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(orow + r * rstride));
+                else *reinterpret_cast<u32x4 *>(orow + r * rstride) = x;
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int64_t grid, bool prefix,
@@ -529,8 +870,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, int32_t head_dim, int64_t g
     switch (head_dim * 2 + (prefix ? 1 : 0)) {
     case 128: hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), g, b, 0, s, a); break;
     case 129: hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), g, b, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), g, b, 0, s, a); break;
-    case 257: hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), g, b, 0, s, a); break;
+    case 256: hipLaunchKernelGGL(prefill_r48_kernel<false>, g, b, 0, s, a); break;
+    case 257: hipLaunchKernelGGL(prefill_r48_kernel<true>, g, b, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

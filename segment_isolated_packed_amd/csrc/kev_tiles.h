@@ -27,22 +27,25 @@ KEV_HD inline int64_t max_items(int64_t total_tokens, int64_t n_seg, int32_t blo
     return (total_tokens + block_rows - 1) / block_rows + n_seg;
 }
 
-// bf16 path: an item of 32*R rows holds G*R (head, 32-row block) units per KV head, one
+// bf16 path: an item of W*R rows holds G*R (head, W-row block) units per KV head, one
 // wavefront each, in workgroups of 4 wavefronts; R is the smallest power of two that makes
-// G*R a multiple of 4.
+// G*R a multiple of 4.  W, the query rows of one wavefront, is 48 for head_dim 128 (three
+// 16-row MFMA blocks) and 32 for head_dim 64.
 struct PrefillShape {
     int32_t row_blocks;     // R
-    int32_t block_rows;     // 32 * R
+    int32_t block_rows;     // W * R
     int32_t wg_per_kvh;     // G * R / 4 workgroups per item and KV head
 };
 
 constexpr int32_t kPrefillUnitsPerWg = 4;   // wavefronts per workgroup
 
-inline PrefillShape prefill_shape_bf16(int32_t heads, int32_t kv_heads) {
+inline int32_t prefill_wave_rows(int32_t head_dim) { return head_dim == 128 ? 48 : 32; }
+
+inline PrefillShape prefill_shape_bf16(int32_t heads, int32_t kv_heads, int32_t head_dim) {
     const int32_t G = heads / kv_heads;
     int32_t r = 1;
     while ((G * r) % kPrefillUnitsPerWg != 0) r *= 2;
-    return PrefillShape{r, 32 * r, G * r / kPrefillUnitsPerWg};
+    return PrefillShape{r, prefill_wave_rows(head_dim) * r, G * r / kPrefillUnitsPerWg};
 }
 
 constexpr int32_t kF32BlockRows = 64;   // fp32 path: one wavefront of 64 rows per item and head

@@ -140,31 +140,35 @@ def test_decode_argument_checks(lib):
 
 
 def test_block_rows(lib):
-    # items of 32*R rows with G*R a multiple of 4 (units fill 4-wavefront workgroups)
-    assert K.kev_prefill_block_rows(28, 4, 128, K.KEV_BF16) == 128    # G=7: R=4, 7 workgroups
-    assert K.kev_prefill_block_rows(32, 8, 128, K.KEV_BF16) == 32     # G=4: R=1, 1 workgroup
-    assert K.kev_prefill_block_rows(12, 2, 128, K.KEV_BF16) == 64     # G=6: R=2, 3 workgroups
-    assert K.kev_prefill_block_rows(4, 4, 128, K.KEV_BF16) == 128     # MHA: R=4
+    # items of W*R rows with G*R a multiple of 4 (units fill 4-wavefront workgroups); W, the
+    # rows of one wavefront, is 48 at head_dim 128 and 32 at head_dim 64
+    assert K.kev_prefill_block_rows(28, 4, 128, K.KEV_BF16) == 192    # G=7: R=4, 7 workgroups
+    assert K.kev_prefill_block_rows(32, 8, 128, K.KEV_BF16) == 48     # G=4: R=1, 1 workgroup
+    assert K.kev_prefill_block_rows(12, 2, 128, K.KEV_BF16) == 96     # G=6: R=2, 3 workgroups
+    assert K.kev_prefill_block_rows(4, 4, 128, K.KEV_BF16) == 192     # MHA: R=4
+    assert K.kev_prefill_block_rows(28, 4, 64, K.KEV_BF16) == 128
+    assert K.kev_prefill_block_rows(32, 8, 64, K.KEV_BF16) == 32
     assert K.kev_prefill_block_rows(4, 4, 16, K.KEV_F32) == 64
+    assert K.kev_prefill_block_rows(4, 4, 128, K.KEV_F32) == 64
     assert K.kev_prefill_block_rows(4, 3, 128, K.KEV_BF16) == 0
 
 
-def covered_pairs(items, cu, block_rows):
+def covered_pairs(items, cu, block_rows, wave_rows):
     """(row, key) pairs the attention kernel evaluates unmasked, per question.
 
-    Mirrors the kernel's visiting rule: a wavefront owns 32 rows of an item and
-    visits 32-key sub-blocks that start before min(its last row + 1, L); inside a
-    sub-block, keys past the row or past the question are masked."""
+    Mirrors the kernel's visiting rule: a wavefront owns wave_rows rows of an item and
+    visits 32-key tiles that start before min(its last row + 1, L); inside a tile, keys
+    past the row or past the question are masked."""
     seen = {}
     for s, t in items:
         a, L = int(cu[s]), int(cu[s + 1] - cu[s])
-        for rb in range(block_rows // 32):
-            row0 = t * block_rows + rb * 32
+        for rb in range(block_rows // wave_rows):
+            row0 = t * block_rows + rb * wave_rows
             if row0 >= L:
                 continue
-            key_end = min(row0 + 32, L)
+            key_end = min(row0 + wave_rows, L)
             for ks in range(0, key_end, 32):
-                for i in range(row0, min(row0 + 32, L)):
+                for i in range(row0, min(row0 + wave_rows, L)):
                     for j in range(ks, min(ks + 32, L)):
                         if j <= i:
                             seen[(a + i, a + j)] = seen.get((a + i, a + j), 0) + 1
@@ -172,8 +176,8 @@ def covered_pairs(items, cu, block_rows):
 
 
 @pytest.mark.parametrize("order", [0, 1])
-@pytest.mark.parametrize("block_rows", [32, 64, 128])
-def test_schedule_covers_each_unmasked_pair_once(block_rows, order):
+@pytest.mark.parametrize("block_rows,wave_rows", [(32, 32), (64, 32), (128, 32), (48, 48), (96, 48), (192, 48)])
+def test_schedule_covers_each_unmasked_pair_once(block_rows, wave_rows, order):
     rng = np.random.default_rng(block_rows + 7 * order)
     for trial in range(4):
         lens = rng.integers(0, 300, size=int(rng.integers(1, 9)))
@@ -195,7 +199,7 @@ def test_schedule_covers_each_unmasked_pair_once(block_rows, order):
             assert (np.diff(items[:, 1]) <= 0).all()
             same_t = items[1:, 1] == items[:-1, 1]
             assert (nb[items[1:, 0]][same_t] <= nb[items[:-1, 0]][same_t]).all()
-        seen = covered_pairs(items, cu, block_rows)
+        seen = covered_pairs(items, cu, block_rows, wave_rows)
         expect = {(int(cu[s]) + i, int(cu[s]) + j) for s in range(len(lens))
                   for i in range(int(lens[s])) for j in range(i + 1)}
         assert set(seen) == expect

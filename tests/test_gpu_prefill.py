@@ -185,7 +185,7 @@ def test_device_schedule_matches_host_schedule():
     for name in ("tiny", "qwen25_7b", "qwen3_8b", "skewed_long"):
         lens = W.prefill_lengths(name)
         cu = W.cu_from_lengths(lens)
-        for br in (32, 64, 128):
+        for br in (32, 48, 64, 96, 128, 192):
             for order in (K.KEV_ORDER_QUESTION, K.KEV_ORDER_LEVEL):
                 say(f"schedule {name} block_rows={br} order={order}")
                 dev = K.kev_schedule_device(to_dev_i32(cu), int(cu[-1]), br, order)
