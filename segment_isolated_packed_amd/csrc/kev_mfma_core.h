@@ -40,14 +40,25 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(1))) const void gbl_void;
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D>
+// LDS row layout of a staged tile: row r's 16-byte chunk c sits at chunk c ^ swz(r).  The
+// LDS has 64 banks of 4 bytes.  Measured with a probe of the bank-conflict counter on
+// gfx950: a 16-byte read serves its lanes in four groups of 16 (lanes with the same bit 5
+// and the same parity of bits 2..4), a transposed 8-byte read (ds_read_b64_tr_b16) in two
+// groups of 32 (lanes 0..31 and 32..63).  The swizzle keeps every group of the kernel's
+// read patterns on distinct banks:
+//   SW = 0: 32 consecutive rows at one chunk (K reads of the 32x32 MFMA) and 4 consecutive
+//           rows x 4 aligned chunks (its transposed V^T reads);
+//   SW = 1 (head_dim 128): rows 0..15 at chunks 4s + g (K reads of the 16x16 MFMA, lane
+//           16g + m reading row m) and 8 consecutive rows x 2 aligned chunks (its
+//           transposed V^T reads).
+template <int D, int SW = 0>
 struct Geom {
     static constexpr int CPR = D / 8;       // 16-byte chunks per row
     static constexpr int RPI = 64 / CPR;    // rows per 1 KB direct-load instruction
     static constexpr int ROWB = D * 2;      // bytes per row
-    // Chunk swizzle: 16 consecutive rows at one chunk (K reads) and 4 consecutive rows
-    // x 4 aligned chunks (transpose reads) both land on distinct 16-byte bank groups.
+    static_assert(SW == 0 || D == 128, "the second swizzle is laid out for head_dim 128");
     __device__ static int swz(int r) {
+        if (SW == 1) return (((r & 7) << 1) | ((r >> 3) & 1)) ^ (r & 8);
         return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((r >> 1) & 7);
     }
     __device__ static int off(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
@@ -97,12 +108,12 @@ __device__ __forceinline__ void dma16s(const void *base, unsigned voff, unsigned
 
 // Per-lane part of a direct load of tile rows [r0, r0 + RPI): the row this lane fills and
 // the global chunk that belongs at its LDS position (chunk c ^ swz(r) of the row).
-template <int D>
+template <int D, int SW = 0>
 struct DmaLane {
     int row;     // tile row (key offset inside the tile)
     int coff;    // element offset of the chunk inside the row
     __device__ void init(int r0) {
-        using G = Geom<D>;
+        using G = Geom<D, SW>;
         const int lane = threadIdx.x & 63;
         row = r0 + lane / G::CPR;
         coff = ((lane % G::CPR) ^ G::swz(row)) * 8;

@@ -130,9 +130,9 @@ struct Cfg {
 //
 // With PREFIX, key index kk < prefix is row kk of the slot's plane (rows D elements apart)
 // and kk >= prefix is row kk - prefix of the packed K/V.
-template <int D, int NW, bool PREFIX>
+template <int D, int NW, bool PREFIX, int SW = 0>
 struct TileLoader {
-    static constexpr int RPI = Geom<D>::RPI;
+    static constexpr int RPI = Geom<D, SW>::RPI;
     static constexpr int IPT = KT / RPI;
     static constexpr int NIT = (IPT + NW - 1) / NW;
     static constexpr int PROW = D * 2;   // bytes per slot row
@@ -157,11 +157,11 @@ struct TileLoader {
         key_end = kend;
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
-            DmaLane<D> ln;
+            DmaLane<D, SW> ln;
             const int r0 = first_row(wave, i);
             ln.init(r0);
             voff[i] = (unsigned)(ln.row * row_bytes + ln.coff * 2);
-            lds_row[i] = (unsigned)(r0 * Geom<D>::ROWB);
+            lds_row[i] = (unsigned)(r0 * Geom<D, SW>::ROWB);
         }
     }
 
@@ -173,7 +173,7 @@ struct TileLoader {
                 const char *tb = pbase + (int64_t)k0 * PROW;
 #pragma unroll
                 for (int i = 0; i < NIT; ++i) {
-                    DmaLane<D> ln;
+                    DmaLane<D, SW> ln;
                     ln.init(first_row(wave, i));
                     dma16s(tb, (unsigned)(ln.row * PROW + ln.coff * 2), stage_addr + lds_row[i]);
                 }
@@ -182,7 +182,7 @@ struct TileLoader {
             if (k0 < prefix) {         // straddles the slot / chunk boundary: per-lane source
 #pragma unroll
                 for (int i = 0; i < NIT; ++i) {
-                    DmaLane<D> ln;
+                    DmaLane<D, SW> ln;
                     ln.init(first_row(wave, i));
                     const int kk = min(k0 + ln.row, key_end - 1);
                     const char *g = kk < prefix ? pbase + (int64_t)kk * PROW + ln.coff * 2
@@ -199,7 +199,7 @@ struct TileLoader {
         } else {
 #pragma unroll
             for (int i = 0; i < NIT; ++i) {
-                DmaLane<D> ln;
+                DmaLane<D, SW> ln;
                 ln.init(first_row(wave, i));
                 const int r = min(k0 + ln.row, key_end - 1) - k0;
                 dma16s(tb, (unsigned)(r * row_bytes + ln.coff * 2), stage_addr + lds_row[i]);
@@ -542,11 +542,14 @@ void prefill_bf16_kernel(PrefillArgs p) {
 // k-slot 8g + 4kb + i is key kb*16 + 4g + i; the V^T operand lists the keys in that same
 // order.  A row's 32 weights of a tile sit in the four lanes m, m+16, m+32, m+48.
 
-// K fragment (kb, s): row kb*16 + m, 16-byte chunk 4s + g (d = 32s + 8g .. +8).  Under the
-// head_dim-128 swizzle its byte offset in a stage is (m*256 + ((g ^ swz(m)) << 4)) ^ (s << 6),
-// plus kb*4096, so one lane base serves all eight fragments.
+// Tiles of this kernel use their own swizzle (Geom<128, 1>), under which the K reads and
+// the transposed V^T reads below are free of bank conflicts.
+//
+// K fragment (kb, s): row kb*16 + m, 16-byte chunk 4s + g (d = 32s + 8g .. +8).  Its byte
+// offset in a stage is (m*256 + ((g ^ swz(m)) << 4)) ^ (s << 6), plus kb*4096 (the swizzle
+// depends on the row only through its low four bits), so one lane base serves all eight.
 __device__ __forceinline__ unsigned k16_lane() {
-    using G = Geom<128>;
+    using G = Geom<128, 1>;
     const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
     return (unsigned)(m * 256 + ((g ^ G::swz(m)) << 4));
 }
@@ -561,7 +564,7 @@ __device__ __forceinline__ bf16x8 k16_frag(const lds_t *stage, unsigned kl, int 
 // (r0*256 + ((((n>>1)&1) ^ swz(r0)) << 4) + (n&1)*8) ^ (db << 5), plus 4096 for the
 // second read (rows 16 apart share the swizzle).
 __device__ __forceinline__ unsigned vt16_lane() {
-    using G = Geom<128>;
+    using G = Geom<128, 1>;
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
     const int r0 = 4 * g + (n >> 2);
     return (unsigned)(r0 * 256 + ((((n >> 1) & 1) ^ G::swz(r0)) << 4) + (n & 1) * 8);
@@ -682,7 +685,7 @@ void prefill_r48_kernel(PrefillArgs p) {
     float c = p.scale_log2;
     asm volatile("" : "+s"(c));
 
-    TileLoader<D, NWAVE, PREFIX> ld;
+    TileLoader<D, NWAVE, PREFIX, 1> ld;
     ld.init(kg, vg, kv_stride, wg_key_end, wave, pk, pv, P);
     auto kaddr = [&](int s) { return lds0 + (unsigned)(s * C::TB); };
     auto vaddr = [&](int s) { return lds0 + (unsigned)((NS + s) * C::TB); };
@@ -835,7 +838,7 @@ void prefill_r48_kernel(PrefillArgs p) {
 #pragma unroll
     for (int rb = 0; rb < 3; ++rb) inv[rb] = 1.f / row_sum4(lrow[rb]);
     if (row0 >= L) return;
-    using GM = Geom<D>;
+    using GM = Geom<D, 1>;
     lds_t *ob = wave < 3 ? kst((n_tiles + 1 + wave) % NS) : vst(n_tiles % NS);
     const int rr = lane / GM::CPR, cc = lane % GM::CPR;
     const int64_t rstride = (int64_t)p.heads * D;
