@@ -37,8 +37,8 @@ PEAK_HBM_GBPS = 8000.0        # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Sources whose change invalidates a kernel's recorded HBM traffic: the kernel itself and
 # everything that decides its launch and item order (the work-list pass and the call).
-PREFILL_SOURCES = ["kev_prefill_bf16.hip", "kev_mfma_core.h", "kev_internal.h", "kev_schedule.hip",
-                   "kev_api.hip"]
+PREFILL_SOURCES = ["kev_prefill_bf16.hip", "kev_mfma_core.h", "kev_internal.h", "kev_tiles.h",
+                   "kev_schedule.hip", "kev_api.hip"]
 DECODE_SOURCES = ["kev_decode.hip", "kev_mfma_core.h", "kev_internal.h", "kev_api.hip"]
 STORE_SOURCES = ["kev_store_kv.hip", "kev_internal.h", "kev_api.hip"]
 PREFILL_NAMES = ("qwen25_7b", "qwen3_8b", "skewed_long")
