@@ -303,18 +303,16 @@ __device__ __forceinline__ void mask_tile(f32x16 &s, int k0, int qrow, int L) {
     }
 }
 
-template <int D, bool PREFIX>
-__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_bf16_kernel(PrefillArgs p) {
-    using C = Cfg<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-    const unsigned lds0 = (unsigned)(uintptr_t)(lds_t *)smem;
-    // K stages at [0, NS*TB), V stages after them.
-    auto kst = [&](int s) { return (lds_t *)smem + s * C::TB; };
-    auto vst = [&](int s) { return (lds_t *)smem + (NS + s) * C::TB; };
+// The work item of this workgroup: record {question start a, length L, query block t,
+// question index sq}, its KV head and its place w among the item's workgroups of that head.
+// The record and the item count are read together (one round trip); records past the count
+// exist (the record array covers the whole grid) and are not used (valid = false).
+struct ItemRef {
+    int a, L, t, sq, kvh, w;
+    bool valid;
+};
 
-    // The item record and the item count are read together (one round trip); records past
-    // the count exist (the record array covers the whole grid) and are not used.
+__device__ __forceinline__ ItemRef prefill_item(const PrefillArgs &p) {
     int item, kvh, w;
     if (p.n_streams > 1) {
         // XCD-aware: this workgroup runs on XCD x and serves one (stream, KV head) pair there,
@@ -328,14 +326,75 @@ void prefill_bf16_kernel(PrefillArgs p) {
         const int per_item = p.kv_heads * p.wg_per_kvh;
         item = blockIdx.x / per_item;
         const int rem = blockIdx.x - item * per_item;
-        kvh = rem % p.kv_heads;   // KV head fastest: see above
+        kvh = rem % p.kv_heads;   // KV head fastest: see Placement
         w = rem / p.kv_heads;
     }
     const __attribute__((address_space(4))) int *recs = (const __attribute__((address_space(4))) int *)p.rec;
-    const int a = recs[4 * item], L = recs[4 * item + 1], t = recs[4 * item + 2], sq = recs[4 * item + 3];
+    ItemRef r;
+    r.a = recs[4 * item];
+    r.L = recs[4 * item + 1];
+    r.t = recs[4 * item + 2];
+    r.sq = recs[4 * item + 3];
+    r.kvh = kvh;
+    r.w = w;
     const int32_t n_items = ((const __attribute__((address_space(4))) int *)p.sched)[0];
-    if (p.n_streams > 1 ? (n_items == 0 || L < 0) : item >= n_items) return;   // past the work list
-    const int rem = w * p.kv_heads + kvh;   // the workgroup's place in its item (0: reports errors)
+    r.valid = p.n_streams > 1 ? (n_items != 0 && r.L >= 0) : item < n_items;
+    return r;
+}
+
+// Chunked prefill: the question continues P rows cached in its slot; pk / pv are that slot's
+// K and V planes of KV head it.kvh.  Returns false, and the first workgroup of the question
+// flags the error, when the slot id or P is out of range (the question's rows are then not
+// written).
+template <int D>
+__device__ __forceinline__ bool slot_prefix(const PrefillArgs &p, const ItemRef &it, int &P, const uint16_t *&pk,
+                                            const uint16_t *&pv) {
+    const int slot = p.slot_ids[it.sq];
+    P = p.prefix_lens[it.sq];
+    const bool bad_slot = slot < 0 || slot >= p.n_slots;
+    if (bad_slot || P < 0 || P > p.capacity - it.L) {
+        if (threadIdx.x == 0 && it.t == 0 && it.w == 0 && it.kvh == 0)
+            atomicOr(p.err, (int32_t)(bad_slot ? KEV_DEVERR_SLOT : KEV_DEVERR_CACHE_LEN));
+        return false;
+    }
+    const int64_t plane = (int64_t)p.capacity * D;
+    pk = static_cast<const uint16_t *>(p.pool) + ((int64_t)slot * 2 * p.kv_heads + it.kvh) * plane;
+    pv = pk + (int64_t)p.kv_heads * plane;
+    return true;
+}
+
+// Runs iteration(j, std::integral_constant<int, j % NS>) for j = 0 .. n_tiles-1, unrolled by
+// the stage count so that every stage index is a compile-time constant.
+template <typename F>
+__device__ __forceinline__ void tile_loop(int n_tiles, F &&iteration) {
+    for (int j0 = 0; j0 < n_tiles; j0 += NS) {
+        iteration(j0, std::integral_constant<int, 0>{});
+        if (j0 + 1 >= n_tiles) break;
+        iteration(j0 + 1, std::integral_constant<int, 1 % NS>{});
+        if (j0 + 2 >= n_tiles) break;
+        iteration(j0 + 2, std::integral_constant<int, 2 % NS>{});
+        if (j0 + 3 >= n_tiles) break;
+        iteration(j0 + 3, std::integral_constant<int, 3 % NS>{});
+        if (NS > 4) {
+            if (j0 + 4 >= n_tiles) break;
+            iteration(j0 + 4, std::integral_constant<int, 4 % NS>{});
+        }
+    }
+}
+
+template <int D, bool PREFIX>
+__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_bf16_kernel(PrefillArgs p) {
+    using C = Cfg<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    const unsigned lds0 = (unsigned)(uintptr_t)(lds_t *)smem;
+    // K stages at [0, NS*TB), V stages after them.
+    auto kst = [&](int s) { return (lds_t *)smem + s * C::TB; };
+    auto vst = [&](int s) { return (lds_t *)smem + (NS + s) * C::TB; };
+
+    const ItemRef it = prefill_item(p);
+    if (!it.valid) return;   // past the work list
+    const int a = it.a, L = it.L, t = it.t, kvh = it.kvh, w = it.w;
     const int G = p.group;
 
     const int item_row0 = t * p.block_rows;
@@ -345,19 +404,8 @@ void prefill_bf16_kernel(PrefillArgs p) {
     // Keys are indexed in the question: P cached rows (chunked prefill), then the L rows here.
     int P = 0;
     const uint16_t *pk = nullptr, *pv = nullptr;
-    if constexpr (PREFIX) {
-        const int slot = p.slot_ids[sq];
-        P = p.prefix_lens[sq];
-        const bool bad_slot = slot < 0 || slot >= p.n_slots;
-        if (bad_slot || P < 0 || P > p.capacity - L) {   // the question's rows are not written
-            if (threadIdx.x == 0 && t == 0 && rem == 0)
-                atomicOr(p.err, (int32_t)(bad_slot ? KEV_DEVERR_SLOT : KEV_DEVERR_CACHE_LEN));
-            return;
-        }
-        const int64_t plane = (int64_t)p.capacity * D;
-        pk = static_cast<const uint16_t *>(p.pool) + ((int64_t)slot * 2 * p.kv_heads + kvh) * plane;
-        pv = pk + (int64_t)p.kv_heads * plane;
-    }
+    if constexpr (PREFIX)
+        if (!slot_prefix<D>(p, it, P, pk, pv)) return;
     const int wg_key_end = P + min(item_row0 + ((NWAVE * w + NWAVE - 1) / G + 1) * 32, L);
     const int n_tiles = (wg_key_end + KT - 1) / KT;
 
@@ -472,23 +520,7 @@ void prefill_bf16_kernel(PrefillArgs p) {
             __builtin_amdgcn_s_setprio(0);
         }
     };
-    for (int j0 = 0; j0 < n_tiles; j0 += NS) {
-        iteration(j0, std::integral_constant<int, 0>{});
-        if (j0 + 1 >= n_tiles) break;
-        iteration(j0 + 1, std::integral_constant<int, 1 % NS>{});
-        if (NS > 2) {
-            if (j0 + 2 >= n_tiles) break;
-            iteration(j0 + 2, std::integral_constant<int, 2 % NS>{});
-        }
-        if (NS > 3) {
-            if (j0 + 3 >= n_tiles) break;
-            iteration(j0 + 3, std::integral_constant<int, 3 % NS>{});
-        }
-        if (NS > 4) {
-            if (j0 + 4 >= n_tiles) break;
-            iteration(j0 + 4, std::integral_constant<int, 4 % NS>{});
-        }
-    }
+    tile_loop(n_tiles, iteration);
 
     wait_vmcnt<0>();   // no direct load may outlive the workgroup's LDS
 
@@ -614,25 +646,9 @@ void prefill_r48_kernel(PrefillArgs p) {
     auto kst = [&](int s) { return (lds_t *)smem + s * C::TB; };
     auto vst = [&](int s) { return (lds_t *)smem + (NS + s) * C::TB; };
 
-    int item, kvh, w;
-    if (p.n_streams > 1) {
-        const int x = blockIdx.x % p.n_xcd, kk = blockIdx.x / p.n_xcd;
-        kvh = x % p.kv_heads;
-        const int idx = kk / p.wg_per_kvh;
-        w = kk - idx * p.wg_per_kvh;
-        item = (x / p.kv_heads) * p.stream_cap + idx;
-    } else {
-        const int per_item = p.kv_heads * p.wg_per_kvh;
-        item = blockIdx.x / per_item;
-        const int rem = blockIdx.x - item * per_item;
-        kvh = rem % p.kv_heads;
-        w = rem / p.kv_heads;
-    }
-    const __attribute__((address_space(4))) int *recs = (const __attribute__((address_space(4))) int *)p.rec;
-    const int a = recs[4 * item], L = recs[4 * item + 1], t = recs[4 * item + 2], sq = recs[4 * item + 3];
-    const int32_t n_items = ((const __attribute__((address_space(4))) int *)p.sched)[0];
-    if (p.n_streams > 1 ? (n_items == 0 || L < 0) : item >= n_items) return;
-    const int rem = w * p.kv_heads + kvh;
+    const ItemRef it = prefill_item(p);
+    if (!it.valid) return;
+    const int a = it.a, L = it.L, t = it.t, kvh = it.kvh, w = it.w;
     const int G = p.group;
 
     const int item_row0 = t * p.block_rows;
@@ -641,19 +657,8 @@ void prefill_r48_kernel(PrefillArgs p) {
 
     int P = 0;
     const uint16_t *pk = nullptr, *pv = nullptr;
-    if constexpr (PREFIX) {
-        const int slot = p.slot_ids[sq];
-        P = p.prefix_lens[sq];
-        const bool bad_slot = slot < 0 || slot >= p.n_slots;
-        if (bad_slot || P < 0 || P > p.capacity - L) {
-            if (threadIdx.x == 0 && t == 0 && rem == 0)
-                atomicOr(p.err, (int32_t)(bad_slot ? KEV_DEVERR_SLOT : KEV_DEVERR_CACHE_LEN));
-            return;
-        }
-        const int64_t plane = (int64_t)p.capacity * D;
-        pk = static_cast<const uint16_t *>(p.pool) + ((int64_t)slot * 2 * p.kv_heads + kvh) * plane;
-        pv = pk + (int64_t)p.kv_heads * plane;
-    }
+    if constexpr (PREFIX)
+        if (!slot_prefix<D>(p, it, P, pk, pv)) return;
     const int wg_key_end = P + min(item_row0 + ((NWAVE * w + NWAVE - 1) / G + 1) * WR, L);
     const int n_tiles = (wg_key_end + KT - 1) / KT;
 
@@ -817,19 +822,7 @@ void prefill_r48_kernel(PrefillArgs p) {
             __builtin_amdgcn_s_setprio(0);
         }
     };
-    for (int j0 = 0; j0 < n_tiles; j0 += NS) {
-        iteration(j0, std::integral_constant<int, 0>{});
-        if (j0 + 1 >= n_tiles) break;
-        iteration(j0 + 1, std::integral_constant<int, 1 % NS>{});
-        if (j0 + 2 >= n_tiles) break;
-        iteration(j0 + 2, std::integral_constant<int, 2 % NS>{});
-        if (j0 + 3 >= n_tiles) break;
-        iteration(j0 + 3, std::integral_constant<int, 3 % NS>{});
-        if (NS > 4) {
-            if (j0 + 4 >= n_tiles) break;
-            iteration(j0 + 4, std::integral_constant<int, 4 % NS>{});
-        }
-    }
+    tile_loop(n_tiles, iteration);
     wait_vmcnt<0>();
 
     // Epilogue: each 16-row block goes through a free stage (the same stages as the 32-row
