@@ -49,6 +49,8 @@ CASES = [
     ([3] * 70, None, 8, 1, 64, 110),                                      # more than 64 questions
     ([5, 40, 1], [100, 0, 31], 32, 1, 64, 160),                           # group of 32, d 64
     ([33, 64], [64, 200], 32, 2, 128, 300),                               # group of 16
+    ([47, 49, 97, 145, 193], [16, 47, 48, 95, 100], 8, 2, 128, 400),     # 48-row block edges (d 128)
+    ([191, 193, 49], [1, 50, 143], 7, 1, 128, 400),                      # 192-row items, group of 7
 ]
 
 

@@ -79,6 +79,15 @@ def test_head_layouts(orc, hq, hk):
     check_full(case, orc, f"bf16 {hq}/{hk} d128 ragged")
 
 
+@pytest.mark.parametrize("hq,hk", [(8, 2), (7, 1), (4, 4), (6, 2)])
+def test_wave_row_block_boundaries(orc, hq, hk):
+    # head_dim 128: a wavefront owns 48 query rows, and an item 48*R rows (R = 1, 4, 4, 4 for
+    # these groupings); lengths on both sides of those edges, every row checked
+    lens = [47, 48, 49, 95, 96, 97, 143, 144, 145, 191, 192, 193, 383, 385]
+    case = W.make_prefill(lens, hq, hk, 128, W.BF16, seed=hq * 7 + hk)
+    check_full(case, orc, f"bf16 {hq}/{hk} d128, 48-row block edges")
+
+
 def test_head_dim_64(orc):
     check_full(W.make_prefill([300, 1, 77, 129], 8, 2, 64, W.BF16, seed=64), orc, "bf16 d64")
 
