@@ -55,6 +55,59 @@ def scratch_users(remarks: str) -> list[tuple[str, int]]:
     return bad
 
 
+def _vregs(operand: str) -> set[int]:
+    m = re.fullmatch(r"v\[(\d+):(\d+)\]", operand)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.fullmatch(r"v(\d+)", operand)
+    return {int(m.group(1))} if m else set()
+
+
+def early_load_reads(asm: str) -> list[tuple[str, str]]:
+    """(kernel, instruction) pairs where a VGPR written by a plain ``global_load_dwordx4`` is read
+    before the first ``s_waitcnt`` on vmcnt that follows it.
+
+    The prefill kernels load their query rows with inline asm, so the compiler adds no wait for
+    them; the counted wait after the K/V prologue covers them.  A copy of one of those registers
+    placed earlier by register allocation would read a load still in flight.
+    """
+    bad, name, pending, done = [], None, set(), False
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            name, pending, done = m.group(1), set(), False
+            continue
+        t = line.strip()
+        if not t or t.startswith((";", ".")) or name is None or done:
+            continue
+        ops = [x.strip(",") for x in t.split()[1:]]
+        if t.startswith("global_load_dwordx4"):
+            pending |= _vregs(ops[0]) if ops else set()
+        elif pending and t.startswith("s_waitcnt") and "vmcnt" in t:
+            done = True
+        elif pending:
+            srcs = set()
+            for o in (ops if t.startswith("s_") else ops[1:]):
+                srcs |= _vregs(o)
+            if srcs & pending:
+                bad.append((name, t))
+    return bad
+
+
+def _check_prefill_asm() -> None:
+    """Compiles the bf16 prefill to device assembly and applies early_load_reads."""
+    asm = os.path.join(OBJ, "kev_prefill_bf16.s")
+    cmd = [hipcc()] + compile_flags() + ["--cuda-device-only", "-S", os.path.join(CSRC, "kev_prefill_bf16.hip"),
+                                         "-o", asm]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for kev_prefill_bf16.hip:\n{p.stderr}")
+    with open(asm) as f:
+        bad = early_load_reads(f.read())
+    if bad:
+        raise RuntimeError(f"kev_prefill_bf16.hip: query-load registers read before their wait: {bad[:4]}")
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc()] + compile_flags() + ["-Rpass-analysis=kernel-resource-usage", "-c",
@@ -70,8 +123,10 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 4)) as ex:
+        check = ex.submit(_check_prefill_asm)
         objs = list(ex.map(_compile, SOURCES))
+        check.result()
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     p = subprocess.run(cmd, capture_output=True, text=True)

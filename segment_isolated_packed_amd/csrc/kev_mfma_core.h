@@ -4,6 +4,9 @@
 //     S^T[key][q]  = K[key][:] . Q[q][:]          (v_mfma_f32_32x32x16_bf16)
 //     O^T[d][q]   += V^T[d][key] . P^T[key][q]
 // with K and V tiles staged in LDS in their natural row-major [key][d] layout.
+// These are the decode's and the head_dim-64 prefill's building blocks; the
+// head_dim-128 prefill runs three 16-row blocks on v_mfma_f32_16x16x32_bf16
+// with its own fragment reads and swizzle (Geom<128, 1>, kev_prefill_bf16.hip).
 //
 // Staging: global_load_lds_dwordx4 writes 64 lanes x 16 B straight into LDS
 // (no VGPR round trip).  A row of D bf16 is D/8 16-byte chunks; chunk c of row

@@ -50,9 +50,10 @@
 // operand reads are described in kev_mfma_core.h and at prefill_r48_kernel.
 //
 // Softmax.  The weights of a tile are taken against the running max as it
-// stands and the max only moves when a lane's tile sum leaves a fixed bound
-// (tile_pv below), so the common tile spends one FMA and one exp per score, a
-// bf16 conversion per pair and a dot product per pair for the row sum.
+// stands and the max only moves when a lane's sum of its weights of the tile
+// leaves a fixed bound (tile_pv, and the per-row move in prefill_r48_kernel),
+// so the common tile spends one FMA and one exp per score, a bf16 conversion
+// per pair and a dot product per pair for the row sum.
 //
 // Pipeline.  Tiles are 32 keys.  K and V each have five LDS stages (80 KB per
 // workgroup, two workgroups per CU fill its 160 KB) and direct loads run four
