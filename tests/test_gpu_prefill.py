@@ -88,6 +88,19 @@ def test_wave_row_block_boundaries(orc, hq, hk):
     check_full(case, orc, f"bf16 {hq}/{hk} d128, 48-row block edges")
 
 
+def test_one_long_question_sampled(orc):
+    # 32768 rows in one question: the last items walk 1024 key tiles
+    case = W.make_prefill([32768], 8, 2, 128, W.BF16, seed=327)
+    say(f"prefill one question of {case.total_tokens} rows, 8/2 heads, sampled")
+    got = to_host_f64(run(case))
+    rows, heads = sample_rows(case, 300, seed=3)
+    rows = np.concatenate([rows, [0, 47, 48, 32767]]).astype(rows.dtype)
+    heads = np.concatenate([heads, [0, 7, 3, 5]]).astype(heads.dtype)
+    ref = orc.prefill_rows(case.q, case.k, case.v, case.cu_seqlens, case.heads, case.kv_heads,
+                           case.head_dim, case.dtype, rows, heads)
+    assert_parity(got[rows, heads], ref, case.dtype, "one 32768-row question, sampled rows")
+
+
 def test_head_dim_64(orc):
     check_full(W.make_prefill([300, 1, 77, 129], 8, 2, 64, W.BF16, seed=64), orc, "bf16 d64")
 
