@@ -34,7 +34,7 @@
 // two item streams instead and each XCD serves one (stream, KV head) pair
 // (PrefillArgs::n_streams), so no two XCDs fetch the same question's K/V.
 //
-// Occupancy.  A workgroup uses 80 KB of LDS and at most 256 registers per lane,
+// Occupancy.  A workgroup uses at most 80 KB of LDS and 256 registers per lane,
 // so two workgroups share each CU and every SIMD runs two wavefronts that belong
 // to different workgroups.  Their barriers are independent, so one wavefront's
 // MFMA work can overlap the other's softmax work.
@@ -55,22 +55,23 @@
 // so the common tile spends one FMA and one exp per score, a bf16 conversion
 // per pair and a dot product per pair for the row sum.
 //
-// Pipeline.  Tiles are 32 keys.  K and V each have five LDS stages (80 KB per
-// workgroup, two workgroups per CU fill its 160 KB) and direct loads run four
-// tiles ahead.  Iteration j starts with the scores of tile j
-// already issued on MFMA.  The wavefront waits for its own loads of K(j+1) and
-// V(j), meets the others at one barrier (which also retires all reads of K(j)
-// and V(j-1), so their stages take K(j+5) and V(j+4)), reads every fragment of
-// V(j) and then K(j+1) into registers at once, takes the softmax of tile j while
-// those reads land, runs P.V of tile j and issues the scores of tile j+1, which
-// execute while it waits at the next barrier.  (The 48-row kernel has no room
-// to hold both fragment sets through the softmax: it reads V(j) after the
-// softmax and K(j+1) after P.V.)  The loop is unrolled by the stage count, so
-// all LDS addresses carry the stage as an immediate offset.  While it issues
-// those MFMAs (16 per tile at 32 rows, 48 at 48 rows) the wavefront holds a
-// raised issue priority, so that when both wavefronts of a SIMD have work
-// ready the one feeding the matrix unit goes first and the other's softmax
-// fills the gaps.  The softmax
+// Pipeline.  Tiles are 32 keys.  K and V each have NS LDS stages and direct
+// loads run NS-1 tiles ahead: five stages (80 KB per workgroup) in the 32-row
+// kernel, four (64 KB) in the 48-row kernel; either way two workgroups share a
+// CU.  Iteration j starts with the scores of tile j already issued on MFMA.
+// The wavefront waits for its own loads of K(j+1) and V(j), meets the others
+// at one barrier (which also retires all reads of K(j) and V(j-1), so their
+// stages take K(j+NS) and V(j+NS-1)), reads every fragment of V(j) and then
+// K(j+1) into registers at once, takes the softmax of tile j while those reads
+// land, runs P.V of tile j and issues the scores of tile j+1, which execute
+// while it waits at the next barrier.  (The 48-row kernel has no room to hold
+// both fragment sets through the softmax: it reads V(j) after the softmax and
+// K(j+1) after P.V.)  The loop is unrolled by the stage count, so all LDS
+// addresses carry the stage as an immediate offset.  In the 32-row kernel the
+// wavefront holds a raised issue priority while it issues its 16 MFMAs of a
+// tile, so that when both wavefronts of a SIMD have work ready the one feeding
+// the matrix unit goes first and the other's softmax fills the gaps; the
+// 48-row kernel ran faster without it (measured on every shape).  The softmax
 // scale is waited for before the loop: a scalar load still in flight there
 // would turn the first use of the scale in every tile into a wait for all
 // outstanding LDS reads (scalar loads return out of order), and the softmax
@@ -105,9 +106,12 @@ using namespace core;
 
 constexpr int KT = 32;      // keys per tile
 constexpr int NWAVE = 4;    // wavefronts per workgroup
-constexpr int NS = 5;       // LDS stages per tensor (loads run NS-1 tiles ahead)
+// LDS stages per tensor (loads run NS-1 tiles ahead): five for the 32-row kernel, four for
+// the 48-row kernel (each measured against the other count on the same box).
+constexpr int NS32 = 5;
+constexpr int NS48 = 4;
 
-template <int D>
+template <int D, int NS>
 struct Cfg {
     static constexpr int DC = D / 16;                    // k steps of the S MFMA
     static constexpr int DB = D / 32;                    // 32-row d blocks of O^T
@@ -366,7 +370,7 @@ __device__ __forceinline__ bool slot_prefix(const PrefillArgs &p, const ItemRef 
 
 // Runs iteration(j, std::integral_constant<int, j % NS>) for j = 0 .. n_tiles-1, unrolled by
 // the stage count so that every stage index is a compile-time constant.
-template <typename F>
+template <int NS, typename F>
 __device__ __forceinline__ void tile_loop(int n_tiles, F &&iteration) {
     for (int j0 = 0; j0 < n_tiles; j0 += NS) {
         iteration(j0, std::integral_constant<int, 0>{});
@@ -386,7 +390,8 @@ __device__ __forceinline__ void tile_loop(int n_tiles, F &&iteration) {
 template <int D, bool PREFIX>
 __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(PrefillArgs p) {
-    using C = Cfg<D>;
+    constexpr int NS = NS32;
+    using C = Cfg<D, NS>;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_t *)smem;
     // K stages at [0, NS*TB), V stages after them.
@@ -521,7 +526,7 @@ void prefill_bf16_kernel(PrefillArgs p) {
             __builtin_amdgcn_s_setprio(0);
         }
     };
-    tile_loop(n_tiles, iteration);
+    tile_loop<NS>(n_tiles, iteration);
 
     wait_vmcnt<0>();   // no direct load may outlive the workgroup's LDS
 
@@ -641,7 +646,8 @@ template <bool PREFIX>
 __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_r48_kernel(PrefillArgs p) {
     constexpr int D = 128, WR = 48;
-    using C = Cfg<D>;
+    constexpr int NS = NS48;
+    using C = Cfg<D, NS>;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_t *)smem;
     auto kst = [&](int s) { return (lds_t *)smem + s * C::TB; };
@@ -806,7 +812,6 @@ void prefill_r48_kernel(PrefillArgs p) {
             const lds_t *vc = vst(uu);
 #pragma unroll
             for (int db = 0; db < 8; ++db) vf[db] = vt16_frag(vc, vl, db);
-            __builtin_amdgcn_s_setprio(3);
 #pragma unroll
             for (int db = 0; db < 8; ++db)
 #pragma unroll
@@ -820,10 +825,9 @@ void prefill_r48_kernel(PrefillArgs p) {
                     for (int s = 0; s < 4; ++s) kf[kb][s] = k16_frag(kn, kl, kb, s);
                 score();
             }
-            __builtin_amdgcn_s_setprio(0);
         }
     };
-    tile_loop(n_tiles, iteration);
+    tile_loop<NS>(n_tiles, iteration);
     wait_vmcnt<0>();
 
     // Epilogue: each 16-row block goes through a free stage (the same stages as the 32-row
