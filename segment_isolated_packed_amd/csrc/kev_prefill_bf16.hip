@@ -170,6 +170,13 @@ struct TileLoader {
         }
     }
 
+    // A tile of the packed stream that ends before key_end (no clamped rows, no slot rows).
+    __device__ __forceinline__ void issue_inner(const char *base, int tile, unsigned stage_addr) const {
+        const char *tb = base + (int64_t)(tile * KT - prefix) * row_bytes;
+#pragma unroll
+        for (int i = 0; i < NIT; ++i) dma16s(tb, voff[i], stage_addr + lds_row[i]);
+    }
+
     __device__ __forceinline__ void issue(const char *base, const char *pbase, int tile, unsigned stage_addr,
                                           int wave) const {
         const int k0 = tile * KT;
@@ -755,11 +762,20 @@ void prefill_r48_kernel(PrefillArgs p) {
 
     auto iteration = [&](const int j, auto U) {
         constexpr int uu = decltype(U)::value;   // j % NS
-        if (j + NS - 1 < n_tiles) wait_vmcnt<2 * C::NIT * (NS - 2)>();
-        else wait_vmcnt<0>();
-        barrier();
-        if (j + NS < n_tiles) ld.issue(ld.kbase, ld.pkbase, j + NS, kaddr(uu), wave);
-        if (j + NS - 1 < n_tiles) ld.issue(ld.vbase, ld.pvbase, j + NS - 1, vaddr((uu + NS - 1) % NS), wave);
+        // both loads of this tile go to tiles before the last one of the workgroup's range (and,
+        // with a slot prefix, past the prefix): no bound checks
+        if (j + NS + 1 < n_tiles && (!PREFIX || (j + NS - 1) * KT >= P)) {
+            wait_vmcnt<2 * C::NIT * (NS - 2)>();
+            barrier();
+            ld.issue_inner(ld.kbase, j + NS, kaddr(uu));
+            ld.issue_inner(ld.vbase, j + NS - 1, vaddr((uu + NS - 1) % NS));
+        } else {
+            if (j + NS - 1 < n_tiles) wait_vmcnt<2 * C::NIT * (NS - 2)>();
+            else wait_vmcnt<0>();
+            barrier();
+            if (j + NS < n_tiles) ld.issue(ld.kbase, ld.pkbase, j + NS, kaddr(uu), wave);
+            if (j + NS - 1 < n_tiles) ld.issue(ld.vbase, ld.pvbase, j + NS - 1, vaddr((uu + NS - 1) % NS), wave);
+        }
         if (j < my_tiles) {
             // lane bases and the mask's lane terms are rebuilt in every tile (one instruction
             // each) rather than kept live across the loop
