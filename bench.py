@@ -10,7 +10,8 @@ the 256 MB MALL.  ``--workload`` selects another prefill shape for the step.
 Prints ONE JSON line.  `value` is the prefill's effective TFLOP/s (only unmasked score
 entries counted: 4 * d * heads * sum L(L+1)/2 FLOPs per call) over the average duration of
 the prefill call (work-list pass + attention kernel) measured with HIP events on the launch
-stream; `roofline.achieved` divides the same FLOPs by the attention kernel's own average
+stream (created without the system-scope fence, so that recording them adds no cache
+write-back and invalidation between the calls); `roofline.achieved` divides the same FLOPs by the attention kernel's own average
 duration, taken with events the library records around that launch on the call's stream.
 The decode's achieved HBM GB/s (algorithmic bytes over event-timed duration) is reported
 beside it, per call and per kernel.  More calls are timed the same way: the other prefill
@@ -69,6 +70,53 @@ def traffic_for(kernel: str, workload: str, src_hash: str):
     if not e or e.get("source_sha256") != src_hash:
         return None
     return e.get("bytes_per_launch")
+
+
+class TimingEvent:
+    """A HIP event used only for timing: created with hipEventDisableSystemFence, so recording it
+    adds no system-scope cache write-back and invalidation between the calls it brackets (HIP
+    documents the flag for events that only measure time).  Same interface as the parts of
+    torch.cuda.Event used here; `cuda_event` is the raw handle the library's kernel-event hook
+    takes."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            import ctypes
+            # the HIP runtime torch has loaded (one runtime per process: its streams are used here)
+            with open("/proc/self/maps") as f:
+                paths = sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+            if not paths:
+                raise RuntimeError("no HIP runtime loaded in this process")
+            h = ctypes.CDLL(paths[0])
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        h = self._runtime()
+        e = ctypes.c_void_p()
+        if h.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self._e = e
+        self.cuda_event = e.value
+
+    def record(self, stream):
+        import ctypes
+        if self._runtime().hipEventRecord(self._e, ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        if self._runtime().hipEventElapsedTime(ctypes.byref(ms), self._e, end._e) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
 
 
 def _sample_pairs(case, rng, n):
@@ -187,14 +235,9 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     def new_events(n, k):
-        """n groups of k timing events, each recorded once so the HIP events exist before
-        their handles are handed to the library."""
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(k)] for _ in range(n)]
-        for g in evs:
-            for e in g:
-                e.record()
+        """n groups of k timing events (TimingEvent: no system-scope fence when recorded)."""
         torch.cuda.synchronize()
-        return evs
+        return [[TimingEvent() for _ in range(k)] for _ in range(n)]
 
     if args.only == "copy":
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
@@ -265,7 +308,7 @@ def main():
     # The main kernels alone (roofline): the same calls again, with events that the library
     # records around that kernel's launch on the call's stream (kept out of the timed steps,
     # whose call times they would lengthen).
-    pre_kernel_ms = dec_kernel_ms = float("nan")
+    pre_kernel_ms = dec_kernel_ms = dec_fenced_ms = float("nan")
     pre_b2b_ms = None
     if do_pre:
         kev = new_events(args.steps, 2)
@@ -279,7 +322,7 @@ def main():
         # throughput a caller issuing prefills one after another sees.
         b2b = []
         for _ in range(5 if args.back_to_back else 0):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = TimingEvent(), TimingEvent()
             e0.record(stream)
             for _ in range(100):
                 K.kev_packed_attn_prefill(q, k, v, cu, out=out)
@@ -296,6 +339,17 @@ def main():
             K.kev_set_kernel_events(None, None)
         torch.cuda.synchronize()
         dec_kernel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in kev]))
+        # The same call between torch's default events, whose recording also writes back and
+        # invalidates the caches at system scope (reported beside the call rate, not as it).
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e in fev:
+            flush()
+            e[0].record(stream)
+            K.kev_slot_attn_decode(dq, dpool, dids, dlens, dkn, dvn, out=dout)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        dec_fenced_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in fev]))
     if K.kev_get_device_errors():
         raise RuntimeError("device error flags in the kernel-timing pass")
 
@@ -519,6 +573,9 @@ def main():
             "decode_seed": dc.seed if dc else None,
             "decode_algorithmic_mb": dbytes / 1e6,
             "step": f"prefill call (scheduler + attention kernel), 512 MiB MALL flush ({args.flush}), decode call",
+            "timing": "HIP events created with hipEventDisableSystemFence around each call and, for the "
+                      "roofline, around each kernel launch (no system-scope cache write-back and "
+                      "invalidation at the events)",
         },
         "prefill_ms": pre_avg,
         "prefill_pct_peak": tflops / PEAK_BF16_TFLOPS * 100 if tflops else None,
@@ -542,6 +599,7 @@ def main():
                          "frac": dec_kernel_gbps / PEAK_HBM_GBPS if dec_kernel_gbps else None,
                          "kernel_ms": dec_kernel_ms,
                          "call_gbps": gbps, "call_frac": gbps / PEAK_HBM_GBPS if gbps else None,
+                         "call_gbps_fenced_events": dbytes / (dec_fenced_ms * 1e6) if dec_fenced_ms == dec_fenced_ms else None,
                          "traffic": traffic_for("decode_bf16_kernel", "slot_decode", source_hash(DECODE_SOURCES)),
                          "kernel": "kev decode_bf16_kernel<128> (the only kernel of the call; kernel "
                                    "events recorded by the library, MALL flushed before each call)",
