@@ -85,9 +85,12 @@ class TimingEvent:
     def _runtime(cls):
         if cls._hip is None:
             import ctypes
-            # the HIP runtime torch has loaded (one runtime per process: its streams are used here)
+            import torch
+            # the HIP runtime torch has loaded: its streams are the ones recorded on here
             with open("/proc/self/maps") as f:
                 paths = sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+            torch_dir = os.path.dirname(os.path.abspath(torch.__file__))
+            paths.sort(key=lambda q: not q.startswith(torch_dir))
             if not paths:
                 raise RuntimeError("no HIP runtime loaded in this process")
             h = ctypes.CDLL(paths[0])
